@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""QSA throughput on one MI355X: one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--graph | --no-graph] [--no-cpu-baseline]
+
+A step is one pass of the whole QSA path over one batch of synthetic input:
+  prefill workloads: key-block compression -> indexer scores + top-k selection
+                     -> block-sparse attention;
+  decode workloads:  indexer scores + top-k over the cached compressed keys ->
+                     block-sparse decode attention (the compressed indexer state
+                     of the cached prefix is computed once, before timing).
+Inputs are resident in HBM before the timed region starts.  ``value`` is
+tokens/s of the whole step (prefill: batch*seq tokens, decode: batch tokens).
+
+``roofline`` describes the dominant kernel (the attention kernel): algorithmic
+flops (prefill, bf16 matrix cores) or algorithmic bytes (decode, HBM) per launch
+divided by its average launch time, measured with events recorded on the stream
+the kernels run on, around every attention launch of the timed steps.
+``cpu_baseline`` times the fp64 oracle (single-threaded BLAS) on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA tokens/s (prefill & decode, 1 GPU); % of HBM / bf16 MFMA roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+DEFAULT_WORKLOAD = "prefill_bf16_4k"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    g = ap.add_mutually_exclusive_group()
+    g.add_argument("--graph", dest="graph", action="store_true", default=True,
+                   help="replay each step's launches from HIP graphs (default)")
+    g.add_argument("--no-graph", dest="graph", action="store_false")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+def prefill_attention_flops(w) -> float:
+    """4 * h_q * d * sum_p |T(p)|, |T(p)| = min(k, n(p)) * B + (p+1) mod B."""
+    p = np.arange(w.seq, dtype=np.int64)
+    n = (p + 1) // w.block
+    tsz = np.minimum(w.top_k, n) * w.block + (p + 1) % w.block
+    return 4.0 * w.h_q * w.d * float(tsz.sum()) * w.batch
+
+
+def decode_attention_bytes(w, lens) -> float:
+    """Selected K and V rows of every KV head + q + out + sel + kv_lens."""
+    esz = 2 if w.dtype == "bf16" else 4
+    L = lens.astype(np.int64)
+    tsz = np.minimum(w.top_k, L // w.block) * w.block + L % w.block
+    kv = float(tsz.sum()) * w.h_kv * w.d * esz * 2
+    return kv + 2.0 * w.batch * w.h_q * w.d * esz + w.batch * w.top_k * 4 + w.batch * 4
+
+
+def kernel_src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_37_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary of this workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != kernel_src_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def setup_prefill(w, dev):
+    import torch
+    from block_sparse_attention_37_amd import qsa as Q
+    from block_sparse_attention_37_amd import synth as S
+    inps = [S.prefill_inputs(w, seq_id=b) for b in range(w.batch)]
+    st = lambda key: torch.stack([S.to_torch(x[key]) for x in inps]).to(dev)
+    plan = Q.PrefillPlan(st("q"), st("k"), st("v"), st("iq"), st("ik"), w.block, w.top_k, w.sm_scale)
+    return plan, inps
+
+
+def setup_decode(w, dev):
+    import torch
+    from block_sparse_attention_37_amd import qsa as Q
+    from block_sparse_attention_37_amd import synth as S
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    lens = S.decode_lens(w)
+    kc = torch.zeros(w.batch, w.max_len, w.h_kv, w.d, dtype=dt, device=dev)
+    vc = torch.zeros_like(kc)
+    ik = torch.zeros(w.batch, w.max_len, w.d_idx, dtype=dt, device=dev)
+    q = torch.zeros(w.batch, w.h_q, w.d, dtype=dt, device=dev)
+    iq = torch.zeros(w.batch, 1, w.h_idx, w.d_idx, dtype=dt, device=dev)
+    for b, s in S.decode_sequences(w, lens):
+        L = int(lens[b])
+        kc[b, :L] = S.to_torch(s["k"]).to(dev)
+        vc[b, :L] = S.to_torch(s["v"]).to(dev)
+        ik[b, :L] = S.to_torch(s["ik"]).to(dev)
+        q[b] = S.to_torch(s["q"]).to(dev)
+        iq[b, 0] = S.to_torch(s["iq"]).to(dev)
+    kvl = torch.from_numpy(lens).to(dev)
+    cmp = Q.compress_keys(ik, w.block, kv_lens=kvl)   # indexer state, not timed
+    del ik
+    plan = Q.DecodePlan(q, kc, vc, kvl, iq, cmp, w.block, w.top_k, w.sm_scale)
+    return plan, lens
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, inps, lens, budget_s: float):
+    """The fp64 oracle on a bounded sample of the workload, single-threaded BLAS."""
+    from threadpoolctl import threadpool_limits
+    import oracle.qsa_oracle as O
+    from block_sparse_attention_37_amd import synth as S
+    t_start = time.perf_counter()
+    with threadpool_limits(limits=1):
+        if w.kind == "prefill":
+            x = inps[0]
+            q, k, v = S.to_f64(x["q"]), S.to_f64(x["k"]), S.to_f64(x["v"])
+            iq, ik = S.to_f64(x["iq"]), S.to_f64(x["ik"])
+            t0 = time.perf_counter()
+            cmp = O.compress_keys(ik, w.block)
+            t_cmp = time.perf_counter() - t0
+            rows = np.random.default_rng(0).permutation(w.seq)
+            done, t_rows = 0, 0.0
+            for p in rows:
+                t0 = time.perf_counter()
+                n = O.candidate_blocks(int(p), w.block)
+                s = O.block_scores(iq[p], cmp, n)
+                sel = O.select_blocks(s, w.top_k)
+                O.attend(q[p], k, v, O.token_set(sel, int(p), w.block), w.sm_scale)
+                t_rows += time.perf_counter() - t0
+                done += 1
+                if time.perf_counter() - t_start > budget_s:
+                    break
+            per_tok = t_rows / done + t_cmp / w.seq
+            sample = (f"compression of all {w.seq} tokens + selection and attention of {done} "
+                      f"randomly chosen query rows of {w.seq}; tokens/s extrapolated per row")
+            value = 1.0 / per_tok
+        else:
+            done, t_seq = 0, 0.0
+            order = np.random.default_rng(0).permutation(w.batch)
+            for b in order:
+                s = S.decode_sequence(w, int(b), int(lens[b]))
+                L = int(lens[b])
+                t0 = time.perf_counter()
+                cmp = O.compress_keys(S.to_f64(s["ik"]), w.block)
+                cmp_t = time.perf_counter() - t0
+                t0 = time.perf_counter()
+                O.decode(S.to_f64(s["q"]), S.to_f64(s["k"]), S.to_f64(s["v"]), L,
+                         S.to_f64(s["iq"]), cmp, w.block, w.top_k, w.sm_scale)
+                t_seq += time.perf_counter() - t0
+                done += 1
+                if time.perf_counter() - t_start > budget_s:
+                    break
+            value = done / t_seq
+            sample = (f"{done} of {w.batch} sequences (selection + attention per new token; the "
+                      f"compressed indexer state is prepared untimed, as on the GPU)")
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": sample}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this QSA build runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        return 2
+    import torch
+    from block_sparse_attention_37_amd import synth as S
+    w = S.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    big = w.name in ("long_prefill_bf16_128k", "long_decode_bf16_b128")
+    steps = args.steps if args.steps is not None else (20 if big else 200)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 20)
+
+    t_setup = time.perf_counter()
+    if w.kind == "prefill":
+        plan, inps = setup_prefill(w, dev)
+        lens = None
+        tokens = w.batch * w.seq
+    else:
+        plan, lens = setup_decode(w, dev)
+        inps = None
+        tokens = w.batch
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+
+    stream = torch.cuda.current_stream(dev)
+    if args.graph:
+        # two graphs per step so that events can bracket the attention launch
+        g_idx, g_att = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        plan.run()  # warm the launch path before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g_idx):
+            plan.run_index()
+        with torch.cuda.graph(g_att):
+            plan.run_attention()
+        torch.cuda.synchronize()
+        run_index, run_attention = g_idx.replay, g_att.replay
+    else:
+        run_index, run_attention = plan.run_index, plan.run_attention
+
+    for _ in range(warmup):
+        run_index()
+        run_attention()
+    torch.cuda.synchronize()
+
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        run_index()
+        ev_a[i].record(stream)
+        run_attention()
+        ev_b[i].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    att_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+    ms_per_step = total_ms / steps
+    value = tokens / (ms_per_step / 1e3)
+
+    if w.kind == "prefill":
+        work = prefill_attention_flops(w)
+        achieved = work / (att_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        work = decode_attention_bytes(w, lens)
+        achieved = work / (att_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = load_traffic(w.name)
+    roof["kernel"] = "qsa::prefill_bf16_kernel" if w.kind == "prefill" else "qsa::decode_bf16_kernel"
+    roof["algorithmic_per_launch"] = work
+    roof["kernel_ms"] = round(att_ms, 5)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inps, lens, args.cpu_seconds)
+
+    cfg = {"workload": w.name, "kind": w.kind, "batch": w.batch, "block": w.block,
+           "top_k": w.top_k, "h_q": w.h_q, "h_kv": w.h_kv, "d": w.d, "h_idx": w.h_idx,
+           "d_idx": w.d_idx, "graph": bool(args.graph)}
+    if w.kind == "prefill":
+        cfg["seq"] = w.seq
+    else:
+        cfg.update(max_len=w.max_len, kv_len_min=int(lens.min()), kv_len_max=int(lens.max()))
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; see block_sparse_attention_37_amd/synth.py)",
+        "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+        "setup_s": round(t_setup, 1),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,45 @@
+// Host-side launchers behind the C ABI (one per kernel family).  Arguments have been
+// validated by the caller; each returns the HIP error of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+hipError_t launch_compress(const void* ik, const int32_t* kv_lens, float* cmp, int batch,
+                           int max_len, int d_idx, int block, bool bf16, hipStream_t stream);
+
+// Largest number of candidate blocks the index kernel can rank per query.
+constexpr int kIndexMaxBlocks = 4096;
+constexpr int kMaxTopK = 256;
+
+hipError_t launch_index_topk(const void* iq, const float* cmp, const int32_t* kv_lens,
+                             int32_t* sel, float* sel_scores, int batch, int n_q, int h_idx,
+                             int d_idx, int max_blocks, int block, int top_k, bool bf16,
+                             hipStream_t stream);
+
+// bf16 prefill on matrix cores.  Returns hipErrorInvalidValue for shapes it is not built for.
+bool prefill_bf16_supported(int group, int d, int block, int top_k, int seq);
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, const int32_t* sel,
+                               void* out, float* lse, int batch, int seq, int h_q, int h_kv,
+                               int d, int block, int top_k, float sm_scale, hipStream_t stream);
+
+// float32 attention (prefill and decode) on the vector ALUs.
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const int32_t* sel,
+                           const int32_t* kv_lens, float* out, float* lse, int batch, int n_q,
+                           int kv_stride_len, int seq_fixed, int h_q, int h_kv, int d, int block,
+                           int top_k, float sm_scale, hipStream_t stream);
+
+// bf16 decode on matrix cores, split over chunks of the selected tokens.
+bool decode_bf16_supported(int group, int d, int block, int top_k);
+int decode_num_splits(int batch, int h_kv, int block, int top_k);
+size_t decode_workspace_bytes(int batch, int h_q, int d, int nsplit);
+hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* kv_lens, const int32_t* sel, void* out, float* lse,
+                              int batch, int max_len, int h_q, int h_kv, int d, int block,
+                              int top_k, float sm_scale, void* workspace, int nsplit,
+                              hipStream_t stream);
+
+}  // namespace qsa

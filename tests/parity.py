@@ -1,0 +1,77 @@
+"""Comparison rules between the HIP path and the fp64 oracle.
+
+Selections (integer results decided by floating-point scores): where the gap
+between the m-th and (m+1)-th best oracle scores exceeds 1e-3 relative, the
+GPU's set must equal the oracle's exactly; inside that band every block
+clearly above the cut must be kept, none clearly below it may be, and the
+count must be m.  Order (ascending) and -1 padding are checked bit-exactly.
+
+Attention outputs: max-abs error <= 2e-2 for bf16 inputs, 1e-4 for float32,
+against the oracle run on the GPU's own selection (so a legitimate choice
+inside a tie band cannot fail the attention check).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle.qsa_oracle as O
+
+TIE_REL = 1e-3
+OUT_ATOL = {"bf16": 2e-2, "f32": 1e-4}
+LSE_ATOL = {"bf16": 2e-3, "f32": 1e-4}
+
+
+def check_selection_row(gpu_row, scores, top_k):
+    """gpu_row: int array [top_k]; scores: oracle fp64 scores of the n
+    candidates.  Returns (ok, in_tie_band, message)."""
+    n = len(scores)
+    m = min(top_k, n)
+    g = np.asarray(gpu_row, dtype=np.int64)
+    if g.shape != (top_k,):
+        return False, False, f"row has shape {g.shape}, expected ({top_k},)"
+    head, tail = g[:m], g[m:]
+    if np.any(tail != -1):
+        return False, False, f"padding not -1: {tail.tolist()}"
+    if m > 1 and np.any(np.diff(head) <= 0):
+        return False, False, f"not strictly ascending: {head.tolist()}"
+    if m and (head.min() < 0 or head.max() >= n):
+        return False, False, f"ids out of [0,{n}): {head.tolist()}"
+    want = O.select_blocks(scores, top_k)
+    if m == n:
+        return bool(np.array_equal(head, want)), False, "all candidates must be kept"
+    srt = np.sort(scores)[::-1]
+    sk, sk1 = srt[m - 1], srt[m]
+    scale = max(abs(sk), abs(sk1))
+    rel = (sk - sk1) / scale if scale > 0 else 0.0
+    if rel > TIE_REL:
+        ok = np.array_equal(head, want)
+        return bool(ok), False, "" if ok else f"set differs outside tie band: {head.tolist()} vs {want.tolist()}"
+    tau = TIE_REL * scale
+    chosen = set(head.tolist())
+    must = set(np.nonzero(scores > sk + tau)[0].tolist())
+    banned = set(np.nonzero(scores < sk - tau)[0].tolist())
+    ok = must <= chosen and not (banned & chosen)
+    return bool(ok), True, "" if ok else "tie-band rule violated"
+
+
+def check_selection(gpu_sel, iq, cmp, kv_len, block, top_k, rows=None):
+    """Check rows of one sequence.  gpu_sel [n_q, top_k]; iq [n_q, Hi, di]
+    float64; cmp oracle float64 compressed keys.  Returns (fails, n_tie)."""
+    n_q = gpu_sel.shape[0]
+    rows = range(n_q) if rows is None else rows
+    fails, ties = [], 0
+    for i in rows:
+        p = kv_len - n_q + i
+        n = O.candidate_blocks(p, block)
+        s = O.block_scores(iq[i], cmp, n)
+        ok, tie, msg = check_selection_row(gpu_sel[i], s, top_k)
+        ties += int(tie)
+        if not ok:
+            fails.append(f"row {i} (p={p}): {msg}")
+    return fails, ties
+
+
+def max_abs(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b))) if a.size else 0.0

@@ -1,0 +1,126 @@
+"""C-ABI library on the host (no GPU needed): it loads, exports every entry
+point declared in include/qsa.h, and rejects bad arguments before launching
+anything.  Pointers passed here are never dereferenced: every call is refused
+by host-side validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_37_amd import qsa as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+INVALID, UNSUPPORTED = 1, 2
+FAKE = 0x10000  # 16-byte aligned, never dereferenced by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_path_calls():
+    names = declared_functions()
+    for n in ("qsa_compress_keys", "qsa_index_topk", "qsa_sparse_attn_prefill",
+              "qsa_sparse_attn_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(qsa_lib):
+    for name in declared_functions():
+        assert hasattr(qsa_lib, name), f"{name} not exported"
+        assert name in Q.SIGNATURES, f"{name} has no binding signature"
+    assert qsa_lib.qsa_version() >= 10000
+
+
+def _err():
+    return Q.lib().qsa_last_error().decode()
+
+
+def test_compress_validation(qsa_lib):
+    L = qsa_lib
+    assert L.qsa_compress_keys(FAKE, None, FAKE, 1, 64, 48, 16, 1, None) == UNSUPPORTED
+    assert "d_idx" in _err()
+    assert L.qsa_compress_keys(FAKE, None, FAKE, -1, 64, 64, 16, 1, None) == INVALID
+    assert L.qsa_compress_keys(FAKE, None, FAKE, 1, 64, 64, 0, 1, None) == INVALID
+    assert L.qsa_compress_keys(None, None, FAKE, 1, 64, 64, 16, 1, None) == INVALID
+    assert "ik" in _err()
+    assert L.qsa_compress_keys(FAKE + 2, None, FAKE, 1, 64, 64, 16, 1, None) == INVALID
+    assert "aligned" in _err()
+    assert L.qsa_compress_keys(FAKE, None, FAKE, 1, 64, 64, 16, 7, None) == INVALID
+    # nothing to do is not an error: no complete block
+    assert L.qsa_compress_keys(FAKE, None, FAKE, 1, 10, 64, 16, 1, None) == 0
+    assert L.qsa_compress_keys(FAKE, None, FAKE, 0, 64, 64, 16, 1, None) == 0
+
+
+def test_index_validation(qsa_lib):
+    L = qsa_lib
+    args = lambda **kw: [kw.get("iq", FAKE), FAKE, kw.get("kvl", None), kw.get("sel", FAKE), None,
+                         kw.get("batch", 1), kw.get("n_q", 256), kw.get("h_idx", 4),
+                         kw.get("d_idx", 64), kw.get("max_blocks", 16), kw.get("block", 16),
+                         kw.get("top_k", 4), 1, None]
+    assert L.qsa_index_topk(*args(top_k=0)) == INVALID
+    assert "top_k" in _err()
+    assert L.qsa_index_topk(*args(max_blocks=15)) == INVALID  # < n_q / block
+    assert L.qsa_index_topk(*args(top_k=257)) == UNSUPPORTED
+    assert L.qsa_index_topk(*args(d_idx=96)) == UNSUPPORTED
+    assert L.qsa_index_topk(*args(max_blocks=5000, n_q=1)) == UNSUPPORTED
+    assert L.qsa_index_topk(*args(sel=None)) == INVALID
+    assert L.qsa_index_topk(*args(n_q=0)) == 0
+
+
+def test_prefill_validation(qsa_lib):
+    L = qsa_lib
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, sel=FAKE, out=FAKE, lse=None, batch=1, seq=128, h_q=8,
+                 h_kv=2, d=128, block=16, top_k=4, scale=0.1, dt=1)
+        a.update(kw)
+        return L.qsa_sparse_attn_prefill(a["q"], a["k"], a["v"], a["sel"], a["out"], a["lse"],
+                                         a["batch"], a["seq"], a["h_q"], a["h_kv"], a["d"],
+                                         a["block"], a["top_k"], a["scale"], a["dt"], None)
+    assert call(h_q=6, h_kv=4) == INVALID
+    assert "multiple" in _err()
+    assert call(top_k=0) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(top_k=300) == UNSUPPORTED
+    assert call(scale=float("nan")) == INVALID
+    assert call(q=None) == INVALID
+    assert call(lse=FAKE + 4) == INVALID
+    assert call(h_q=48, h_kv=1) == UNSUPPORTED  # group 48 not built for bf16
+    assert call(seq=0) == 0
+
+
+def test_decode_validation(qsa_lib):
+    L = qsa_lib
+    n = ctypes.c_size_t(0)
+    assert L.qsa_sparse_attn_decode_workspace_size(64, 32, 4, 128, 64, 32, ctypes.byref(n)) == 0
+    need = n.value
+    assert need > 0  # 256 (sequence, KV head) pairs -> split work -> workspace
+    assert L.qsa_sparse_attn_decode_workspace_size(64, 32, 4, 128, 64, 32, None) == INVALID
+    def call(**kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, kvl=FAKE, sel=FAKE, out=FAKE, lse=None, batch=64,
+                 max_len=32768, h_q=32, h_kv=4, d=128, block=64, top_k=32, scale=0.1, ws=FAKE,
+                 wsb=need, dt=1)
+        a.update(kw)
+        return L.qsa_sparse_attn_decode(a["q"], a["kc"], a["vc"], a["kvl"], a["sel"], a["out"],
+                                        a["lse"], a["batch"], a["max_len"], a["h_q"], a["h_kv"],
+                                        a["d"], a["block"], a["top_k"], a["scale"], a["ws"],
+                                        a["wsb"], a["dt"], None)
+    assert call(wsb=need - 1) == INVALID
+    assert "workspace" in _err()
+    assert call(ws=None) == INVALID
+    assert call(kvl=None) == INVALID
+    assert call(h_q=30) == INVALID
+    assert call(h_q=64, h_kv=2) == UNSUPPORTED  # group 32 > 16 not built for bf16 decode
+    assert call(batch=0) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        Q.compress_keys(x, 16)

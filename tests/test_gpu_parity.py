@@ -1,0 +1,323 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Sizes: small shapes that span several tiles, blocks and a ragged tail; the two
+small workloads in full; the long workloads at full size on sampled rows /
+sequences (selection on a stratified sample, attention on fewer rows).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.qsa_oracle as O
+from block_sparse_attention_37_amd import qsa as Q
+from block_sparse_attention_37_amd import synth as S
+from parity import LSE_ATOL, OUT_ATOL, check_selection, max_abs
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _t(a, dev):
+    return S.to_torch(a, dev)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def gpu_prefill(w, inps, dev):
+    """inps: list over batch of synth.prefill_inputs dicts."""
+    st = lambda key: torch.stack([_t(x[key], dev) for x in inps])
+    q, k, v, iq, ik = st("q"), st("k"), st("v"), st("iq"), st("ik")
+    cmp = Q.compress_keys(ik, w.block)
+    sel, sc = Q.index_topk(iq, cmp, w.block, w.top_k, with_scores=True)
+    out, lse = Q.sparse_attn_prefill(q, k, v, sel, w.block, w.sm_scale, return_lse=True)
+    torch.cuda.synchronize()
+    return dict(cmp=cmp.cpu().numpy(), sel=sel.cpu().numpy(), sc=sc.cpu().numpy(),
+                out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+
+
+def check_prefill(w, inp, res, b=0, rows=None, sel_rows=None, exact_ties=False):
+    T, B = w.seq, w.block
+    q64, k64, v64 = S.to_f64(inp["q"]), S.to_f64(inp["k"]), S.to_f64(inp["v"])
+    iq64, ik64 = S.to_f64(inp["iq"]), S.to_f64(inp["ik"])
+    cmp_o = O.compress_keys(ik64, B)
+    assert res["cmp"][b].shape == cmp_o.shape
+    err = max_abs(res["cmp"][b], cmp_o)
+    assert err <= 1e-5, f"compressed keys differ by {err}"
+    fails, ties = check_selection(res["sel"][b], iq64, cmp_o, T, B, w.top_k, rows=sel_rows)
+    assert not fails, "\n".join(fails[:5])
+    # selected scores (float32 on the GPU) against the oracle's fp64 scores
+    chk = range(T) if sel_rows is None else sel_rows
+    for i in list(chk)[:: max(1, len(list(chk)) // 64)]:
+        ids = [j for j in res["sel"][b][i] if j >= 0]
+        s = O.block_scores(iq64[i], cmp_o, O.candidate_blocks(i, B))
+        if ids:
+            scale = max(1.0, float(np.abs(s).max()))
+            assert max_abs(res["sc"][b][i][: len(ids)], s[ids]) <= 1e-4 * scale
+    rows = range(T) if rows is None else rows
+    rows = list(rows)
+    out_o, lse_o = O.attend_rows(q64, k64, v64, res["sel"][b], np.arange(T), rows, B, w.sm_scale)
+    e_out = max_abs(res["out"][b][rows], out_o)
+    e_lse = max_abs(res["lse"][b][rows], lse_o)
+    say(f"  {w.name}: rows={len(rows)} tie-band rows={ties} out err={e_out:.3g} lse err={e_lse:.3g}")
+    assert e_out <= OUT_ATOL[w.dtype], f"out max-abs error {e_out}"
+    assert e_lse <= LSE_ATOL[w.dtype], f"lse max-abs error {e_lse}"
+    return ties
+
+
+def _wl(name, **kw):
+    base = dict(seed=100, kind="prefill", dtype="bf16", batch=1, h_idx=2, d_idx=32)
+    base.update(kw)
+    return S.Workload(name, **base)
+
+
+EDGE_PREFILL = [
+    _wl("g8_d128_b16", seq=37, block=16, top_k=2, h_q=8, h_kv=1, d=128),
+    _wl("shorter_than_block", seq=15, block=16, top_k=2, h_q=8, h_kv=1, d=128),
+    _wl("one_token", seq=1, block=16, top_k=1, h_q=8, h_kv=1, d=64),
+    _wl("k_covers_all_dense", seq=256, block=64, top_k=8, h_q=8, h_kv=2, d=64, h_idx=4, d_idx=64),
+    _wl("block100_two_subchunks", seq=300, block=100, top_k=1, h_q=16, h_kv=1, d=128),
+    _wl("g2_d64_b32", seq=200, block=32, top_k=3, h_q=4, h_kv=2, d=64, d_idx=128, h_idx=3),
+    _wl("g1_tile_spans_blocks", seq=129, block=16, top_k=4, h_q=2, h_kv=2, d=128),
+    _wl("g32", seq=70, block=16, top_k=2, h_q=32, h_kv=1, d=64),
+    _wl("g16_exact_multiple", seq=256, block=32, top_k=3, h_q=16, h_kv=1, d=128),
+    _wl("many_tiles_ragged", seq=1000, block=64, top_k=4, h_q=16, h_kv=2, d=128, h_idx=8,
+        d_idx=64, query_mean=True, plant_frac=0.1),
+    _wl("f32_small", seq=77, block=8, top_k=3, h_q=4, h_kv=2, d=64, dtype="f32"),
+    _wl("f32_d128", seq=40, block=16, top_k=1, h_q=2, h_kv=1, d=128, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("w", EDGE_PREFILL, ids=lambda w: w.name)
+def test_prefill_edge_shapes(gpu, w):
+    say(f"case prefill {w.name}")
+    inp = S.prefill_inputs(w)
+    res = gpu_prefill(w, [inp], gpu)
+    check_prefill(w, inp, res)
+
+
+def test_prefill_batch2(gpu):
+    w = _wl("batch2", seq=150, block=16, top_k=3, h_q=8, h_kv=2, d=128, batch=2)
+    say("case prefill batch2")
+    inps = [S.prefill_inputs(w, seq_id=b) for b in range(2)]
+    res = gpu_prefill(w, inps, gpu)
+    for b in range(2):
+        check_prefill(w, inps[b], res, b=b)
+
+
+def test_prefill_dense_equivalence(gpu):
+    """top_k >= number of blocks: QSA equals causal dense attention (torch, fp32 CPU)."""
+    w = _wl("dense", seq=200, block=16, top_k=13, h_q=8, h_kv=2, d=128)
+    say("case prefill dense equivalence")
+    inp = S.prefill_inputs(w)
+    res = gpu_prefill(w, [inp], gpu)
+    q = torch.from_numpy(S.to_f64(inp["q"])).float().permute(1, 0, 2)[None]
+    k = torch.from_numpy(S.to_f64(inp["k"])).float().permute(1, 0, 2)[None]
+    v = torch.from_numpy(S.to_f64(inp["v"])).float().permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, is_causal=True, scale=w.sm_scale, enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    assert max_abs(res["out"][0], ref) <= OUT_ATOL["bf16"]
+
+
+def test_prefill_exact_ties_lowest_index(gpu):
+    """All compressed keys equal -> all scores equal -> blocks 0..m-1 kept."""
+    w = _wl("ties", seq=160, block=16, top_k=3, h_q=8, h_kv=1, d=64)
+    inp = S.prefill_inputs(w)
+    inp["ik"] = np.full_like(inp["ik"], S.bf16_bits(np.ones(1, np.float32))[0])
+    res = gpu_prefill(w, [inp], gpu)
+    for p in range(w.seq):
+        n = O.candidate_blocks(p, w.block)
+        m = min(w.top_k, n)
+        want = list(range(m)) + [-1] * (w.top_k - m)
+        assert res["sel"][0][p].tolist() == want, f"row {p}"
+    check_prefill(w, inp, res)
+
+
+def test_tiny_prefill_f32_full(gpu):
+    w = S.WORKLOADS["tiny_prefill_f32"]
+    say(f"case {w.name}")
+    inp = S.prefill_inputs(w)
+    res = gpu_prefill(w, [inp], gpu)
+    check_prefill(w, inp, res)
+    # k = 16 >= 15 blocks: dense causal equivalence on the same inputs
+    wd = w.with_(top_k=16)
+    resd = gpu_prefill(wd, [inp], gpu)
+    check_prefill(wd, inp, resd)
+
+
+def test_prefill_bf16_4k_full(gpu):
+    w = S.WORKLOADS["prefill_bf16_4k"]
+    say(f"case {w.name}")
+    inp = S.prefill_inputs(w)
+    res = gpu_prefill(w, [inp], gpu)
+    check_prefill(w, inp, res)
+
+
+def test_prefill_deterministic(gpu):
+    w = S.WORKLOADS["prefill_bf16_4k"]
+    inp = S.prefill_inputs(w)
+    a = gpu_prefill(w, [inp], gpu)
+    b = gpu_prefill(w, [inp], gpu)
+    for key in ("cmp", "sel", "sc", "out", "lse"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+def _stratified_rows(T, B, count, seed):
+    rows = set(range(min(T, 2 * B)))
+    rows |= {p for p in range(max(0, T - 8 * B), T) if (p + 1) % B == 0}
+    rows |= {T - 1, T - 2}
+    r = np.random.default_rng(seed)
+    rows |= set(r.choice(T, size=min(T, count), replace=False).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.slow
+def test_long_prefill_bf16_128k_sampled(gpu):
+    w = S.WORKLOADS["long_prefill_bf16_128k"]
+    say(f"case {w.name}: generating inputs")
+    inp = S.prefill_inputs(w)
+    say("  running GPU path")
+    res = gpu_prefill(w, [inp], gpu)
+    sel_rows = _stratified_rows(w.seq, w.block, 6000, 7)
+    att_rows = _stratified_rows(w.seq, w.block, 200, 8)
+    att_rows = [r for r in att_rows if r < 64 or r % 3 == 0 or (r + 1) % w.block == 0][:400]
+    check_prefill(w, inp, res, rows=att_rows, sel_rows=sel_rows)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def gpu_decode_setup(w, lens, dev, seqs=None):
+    """Fill caches on the GPU sequence by sequence; returns tensors and the
+    host copies of the sequences listed in ``seqs`` (for the oracle)."""
+    kc = torch.zeros(w.batch, w.max_len, w.h_kv, w.d, dtype=torch.bfloat16 if w.dtype == "bf16"
+                     else torch.float32, device=dev)
+    vc = torch.zeros_like(kc)
+    ik = torch.zeros(w.batch, w.max_len, w.d_idx, dtype=kc.dtype, device=dev)
+    q = torch.zeros(w.batch, w.h_q, w.d, dtype=kc.dtype, device=dev)
+    iq = torch.zeros(w.batch, w.h_idx, w.d_idx, dtype=kc.dtype, device=dev)
+    keep = {}
+    for b, s in S.decode_sequences(w, lens):
+        L = int(lens[b])
+        kc[b, :L] = _t(s["k"], dev)
+        vc[b, :L] = _t(s["v"], dev)
+        ik[b, :L] = _t(s["ik"], dev)
+        q[b] = _t(s["q"], dev)
+        iq[b] = _t(s["iq"], dev)
+        if seqs is None or b in seqs:
+            keep[b] = s
+    return q, kc, vc, ik, iq, keep
+
+
+def gpu_decode(w, lens, tensors):
+    q, kc, vc, ik, iq = tensors
+    dev = q.device
+    kvl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    cmp = Q.compress_keys(ik, w.block, kv_lens=kvl)  # indexer state of the cached prefix
+    sel, sc = Q.index_topk(iq.reshape(w.batch, 1, w.h_idx, w.d_idx), cmp, w.block, w.top_k,
+                           kv_lens=kvl, with_scores=True)
+    out, lse = Q.sparse_attn_decode(q, kc, vc, kvl, sel, w.block, w.sm_scale, return_lse=True)
+    torch.cuda.synchronize()
+    return dict(cmp=cmp.cpu().numpy(), sel=sel.reshape(w.batch, w.top_k).cpu().numpy(),
+                out=out.float().cpu().numpy(), lse=lse.cpu().numpy())
+
+
+def check_decode(w, lens, res, keep):
+    worst = 0.0
+    ties = 0
+    for b, s in keep.items():
+        L = int(lens[b])
+        ik64 = S.to_f64(s["ik"])
+        cmp_o = O.compress_keys(ik64, w.block)
+        assert max_abs(res["cmp"][b][: len(cmp_o)], cmp_o) <= 1e-5
+        fails, t = check_selection(res["sel"][b][None], S.to_f64(s["iq"])[None], cmp_o, L,
+                                   w.block, w.top_k)
+        ties += t
+        assert not fails, f"seq {b}: {fails}"
+        toks = O.token_set([j for j in res["sel"][b] if j >= 0], L - 1, w.block)
+        out_o, lse_o = O.attend(S.to_f64(s["q"]), S.to_f64(s["k"]), S.to_f64(s["v"]), toks,
+                                w.sm_scale)
+        e = max_abs(res["out"][b], out_o)
+        worst = max(worst, e)
+        assert e <= OUT_ATOL[w.dtype], f"seq {b}: out error {e}"
+        assert max_abs(res["lse"][b], lse_o) <= LSE_ATOL[w.dtype], f"seq {b}: lse"
+    say(f"  {w.name}: seqs={len(keep)} tie-band={ties} worst out err={worst:.3g}")
+
+
+def _dw(name, **kw):
+    base = dict(seed=200, kind="decode", dtype="bf16", h_idx=2, d_idx=32)
+    base.update(kw)
+    return S.Workload(name, **base)
+
+
+EDGE_DECODE = [
+    (_dw("ragged_small", batch=5, max_len=300, block=16, top_k=3, h_q=8, h_kv=1, d=128),
+     [1, 16, 17, 64, 300]),
+    (_dw("g16_d64", batch=3, max_len=512, block=64, top_k=2, h_q=16, h_kv=1, d=64),
+     [63, 64, 500]),
+    (_dw("g4_block100", batch=2, max_len=1000, block=100, top_k=4, h_q=8, h_kv=2, d=128),
+     [999, 450]),
+    (_dw("g1", batch=2, max_len=256, block=32, top_k=8, h_q=2, h_kv=2, d=128), [256, 200]),
+    (_dw("f32", batch=3, max_len=200, block=16, top_k=2, h_q=4, h_kv=2, d=64, dtype="f32"),
+     [5, 100, 200]),
+    (_dw("wide_split", batch=1, max_len=8192, block=64, top_k=64, h_q=8, h_kv=1, d=128),
+     [8000]),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_DECODE, ids=lambda c: c[0].name)
+def test_decode_edge_shapes(gpu, case):
+    w, lens = case
+    lens = np.array(lens, dtype=np.int32)
+    say(f"case decode {w.name} lens={lens.tolist()}")
+    *tensors, keep = gpu_decode_setup(w, lens, gpu)
+    res = gpu_decode(w, lens, tensors)
+    check_decode(w, lens, res, keep)
+
+
+def test_decode_matches_prefill_rows(gpu):
+    """Decode at kv_len = p+1 reproduces prefill row p (both on the GPU)."""
+    w = _wl("pd", seq=300, block=32, top_k=3, h_q=8, h_kv=2, d=128)
+    inp = S.prefill_inputs(w)
+    res = gpu_prefill(w, [inp], gpu)
+    rows = [0, 30, 31, 32, 63, 200, 255, 299]
+    for p in rows:
+        L = p + 1
+        qd = _t(inp["q"][p], gpu)[None]
+        kc = _t(inp["k"], gpu)[None]
+        vc = _t(inp["v"], gpu)[None]
+        kvl = torch.tensor([L], dtype=torch.int32, device=gpu)
+        cmp = Q.compress_keys(_t(inp["ik"], gpu)[None], w.block, kv_lens=kvl)
+        sel = Q.index_topk(_t(inp["iq"][p], gpu)[None, None], cmp, w.block, w.top_k, kv_lens=kvl)
+        out = Q.sparse_attn_decode(qd, kc, vc, kvl, sel, w.block, w.sm_scale)
+        torch.cuda.synchronize()
+        assert sel.cpu().numpy()[0, 0].tolist() == res["sel"][0][p].tolist(), f"row {p}"
+        assert max_abs(out.float().cpu().numpy()[0], res["out"][0][p]) <= 2e-2
+
+
+def test_decode_bf16_b64_full(gpu):
+    w = S.WORKLOADS["decode_bf16_b64"]
+    lens = S.decode_lens(w)
+    say(f"case {w.name}: generating")
+    *tensors, keep = gpu_decode_setup(w, lens, gpu)
+    res = gpu_decode(w, lens, tensors)
+    check_decode(w, lens, res, keep)
+
+
+@pytest.mark.slow
+def test_long_decode_bf16_b128_sampled(gpu):
+    w = S.WORKLOADS["long_decode_bf16_b128"]
+    lens = S.decode_lens(w)
+    seqs = {0, 1, 63, 64, 126, 127}
+    say(f"case {w.name}: generating 34 GB of caches")
+    *tensors, keep = gpu_decode_setup(w, lens, gpu, seqs=seqs)
+    say("  running GPU path")
+    res = gpu_decode(w, lens, tensors)
+    check_decode(w, lens, res, keep)
