@@ -120,6 +120,8 @@ def setup_decode(w, dev):
     q = torch.zeros(w.batch, w.h_q, w.d, dtype=dt, device=dev)
     iq = torch.zeros(w.batch, 1, w.h_idx, w.d_idx, dtype=dt, device=dev)
     for b, s in S.decode_sequences(w, lens):
+        if b % 16 == 0:
+            print(f"[bench] generating decode inputs: sequence {b}/{w.batch}", file=sys.stderr, flush=True)
         L = int(lens[b])
         kc[b, :L] = S.to_torch(s["k"]).to(dev)
         vc[b, :L] = S.to_torch(s["v"]).to(dev)

@@ -137,10 +137,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   {
     const uint16_t* qp = q + (((size_t)b * seq + (valid_row ? p : 0)) * h_q + hh) * D + half * 8;
 #pragma unroll
-    for (int t = 0; t < NKS; ++t) {
-      u32x4 w = valid_row ? *reinterpret_cast<const u32x4*>(qp + t * 16) : u32x4{0u, 0u, 0u, 0u};
-      qreg[t] = bitcast<bf16x8>(w);
-    }
+    for (int t = 0; t < NKS; ++t) qreg[t] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(qp + t * 16));
   }
 
   int ptr = 0;
@@ -156,11 +153,19 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
 
   const int nsub = (block + KC - 1) / KC;
-  const size_t kv_row = (size_t)h_kv * D;  // elements between consecutive tokens
+  const uint32_t kv_row = (uint32_t)h_kv * D;  // elements between consecutive tokens
   const uint16_t* kbase = k + ((size_t)b * seq * h_kv + g) * D;
   const uint16_t* vbase = v + ((size_t)b * seq * h_kv + g) * D;
 
-  u32x4 kreg[KIT];
+  // K goes global -> LDS directly (no registers): wave-instruction i fills rows
+  // i*(256/NC16) + wave*RPI .. +RPI-1, lane -> (row lane/NC16, physical chunk lane%NC16),
+  // so the lane fetches the logical chunk that the XOR swizzle maps to that slot.
+  constexpr int RPI = 64 / NC16;
+  const int wave_u = wave_uniform(wave);
+  const int k_lrow = lane / NC16;
+  const int k_pc = lane % NC16;
+  // V rows vq*4+i (chunk vc) are staged in registers and written transposed.
+  const int vc = tid % NC16, vq = tid / NC16;
   u32x4 vreg[4];
 
   auto chunk_keys = [&](const ChunkIter& it, int& key0, int& ck) {
@@ -169,50 +174,37 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     ck = min(ck, seq - key0);
   };
 
-  auto load_chunk = [&](const ChunkIter& it) {
-    int key0, ck;
-    chunk_keys(it, key0, ck);
+  // Rows past the chunk are clamped into the tensor; their keys are masked.
+  auto load_chunk = [&](const ChunkIter& it, int buf) {
+    const int key0 = it.j * block + it.sub * KC;
 #pragma unroll
     for (int i = 0; i < KIT; ++i) {
-      const int e = i * 256 + tid;
-      const int r = e / NC16, c = e % NC16;
-      kreg[i] = (r < ck) ? *reinterpret_cast<const u32x4*>(kbase + (size_t)(key0 + r) * kv_row + c * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
+      const int r = i * (256 / NC16) + wave_u * RPI + k_lrow;
+      const int c = k_pc ^ (r & (NC16 - 1));
+      const uint32_t row = (uint32_t)min(key0 + r, seq - 1);
+      global_to_lds16(kbase + row * kv_row + c * 8, &Ks[buf][(i * (256 / NC16) + wave_u * RPI) * D]);
     }
     if (tid < VQ) {
-      const int c = tid % NC16, quad = tid / NC16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = quad * 4 + i;
-        vreg[i] = (r < ck) ? *reinterpret_cast<const u32x4*>(vbase + (size_t)(key0 + r) * kv_row + c * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t row = (uint32_t)min(key0 + vq * 4 + i, seq - 1);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + row * kv_row + vc * 8);
       }
     }
   };
 
   auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KIT; ++i) {
-      const int e = i * 256 + tid;
-      const int r = e / NC16, c = e % NC16;
-      *reinterpret_cast<u32x4*>(&Ks[buf][r * D + ((c ^ (r & (NC16 - 1))) * 8)]) = kreg[i];
-    }
     if (tid < VQ) {
-      const int c = tid % NC16, quad = tid / NC16;
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int d = c * 8 + dd;
-        const int w = dd >> 1;
-        uint32_t lo, hi;
-        if (dd & 1) {
-          lo = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
-          hi = (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u);
-        } else {
-          lo = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
-          hi = (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16);
-        }
-        const int unit = quad ^ ((d >> 1) & 15);
-        *reinterpret_cast<u32x2*>(&Vt[buf][d * KC + unit * 4]) = u32x2{lo, hi};
+      for (int w = 0; w < 4; ++w) {
+        // element pairs (2w, 2w+1) of the 4 rows -> V^T rows d = vc*8 + 2w, +1
+        const uint32_t e0lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
+        const uint32_t e0hi = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
+        const uint32_t e1lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
+        const uint32_t e1hi = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
+        const int d0 = vc * 8 + 2 * w, d1 = d0 + 1;
+        *reinterpret_cast<u32x2*>(&Vt[buf][d0 * KC + ((vq ^ ((d0 >> 1) & 15)) * 4)]) = u32x2{e0lo, e0hi};
+        *reinterpret_cast<u32x2*>(&Vt[buf][d1 * KC + ((vq ^ ((d1 >> 1) & 15)) * 4)]) = u32x2{e1lo, e1hi};
       }
     }
   };
@@ -220,16 +212,18 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   ChunkIter cur{0, bm[0], -1, 0};
   bool have = next_block(bm, words, cur);
   if (have) {
-    load_chunk(cur);
+    load_chunk(cur, 0);
     store_chunk(0);
   }
+  wait_all_memory();  // LDS-direct loads are counted by vmcnt
   __syncthreads();
   int buf = 0;
+  const float ninf = -__builtin_inff();
 
   while (have) {
     ChunkIter nxt = cur;
     const bool have_next = advance(bm, words, nsub, nxt);
-    if (have_next) load_chunk(nxt);
+    if (have_next) load_chunk(nxt, buf ^ 1);
 
     if (cur.sub == 0) {
       const bool hit = (cur_sel == cur.j);
@@ -243,82 +237,83 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     if (__ballot(vis) != 0ull) {
       int key0, ck;
       chunk_keys(cur, key0, ck);
-      const int nkt = ck > 32 ? 2 : 1;
-      f32x16 S[2];
+      const bool emask = ck < KC || key0 + KC - 1 > p0;  // keys past the chunk or after p
+      // one 32-key tile at a time: S^T tile -> online softmax -> P^T -> O^T update
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        if (kt < nkt) {
-          f32x16 acc;
+        if (kt == 1 && ck <= 32) break;
+        f32x16 S;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        for (int r = 0; r < 16; ++r) S[r] = 0.f;
+        {
           const int kr = kt * 32 + row;
 #pragma unroll
           for (int t = 0; t < NKS; ++t) {
             const int c = t * 2 + half;
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[buf][kr * D + ((c ^ (kr & (NC16 - 1))) * 8)]);
-            acc = mfma32x32x16(a, qreg[t], acc);
+            S = mfma32x32x16(a, qreg[t], S);
           }
-          S[kt] = acc;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) S[kt][r] = -__builtin_inff();
         }
-      }
-      // scale, mask, running max
-      float mx = -__builtin_inff();
+        if (emask) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          float x = S[kt][r] * scale_log2;
-          if (!vis || kr >= ck || key0 + kr > p) x = -__builtin_inff();
-          S[kt][r] = x;
-          mx = fmaxf(mx, x);
+          for (int r = 0; r < 16; ++r) {
+            const int kr = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (kr >= ck || key0 + kr > p) S[r] = ninf;
+          }
         }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float psum = 0.f;
-      bf16x8 P[4];
+        float mx = ninf;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        u32x4 w;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // the running max moves only when it grows by more than 8 (log2 units): rare
+        // rescales, and every exponent below stays <= 8
+        const float m_cand = vis ? fmaxf(m_run, mx * scale_log2) : m_run;
+        const bool need = m_cand > m_run + 8.0f;
+        if (__ballot(need) != 0ull) {
+          const float m_new = need ? m_cand : m_run;
+          // lanes that keep their max (possibly still -inf) keep their state exactly
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float e0 = __builtin_amdgcn_exp2f(S[u >> 1][8 * (u & 1) + 2 * jj] - m_use);
-          const float e1 = __builtin_amdgcn_exp2f(S[u >> 1][8 * (u & 1) + 2 * jj + 1] - m_use);
-          psum += e0 + e1;
-          w[jj] = pack_bf16x2(e0, e1);
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
         }
-        P[u] = bitcast<bf16x8>(w);
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+        const float nb = (vis && m_run != ninf) ? -m_run : ninf;
+        float psum = 0.f;
+        bf16x8 P[2];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+        for (int uu = 0; uu < 2; ++uu) {
+          u32x4 w;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-
+          for (int jj = 0; jj < 4; ++jj) {
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * uu + 2 * jj], scale_log2, nb));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * uu + 2 * jj + 1], scale_log2, nb));
+            psum += e0 + e1;
+            w[jj] = pack_bf16x2(e0, e1);
+          }
+          P[uu] = bitcast<bf16x8>(w);
+        }
+        l_run += psum;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int d = dt * 32 + row;
-        const int sw = (d >> 1) & 15;
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d = dt * 32 + row;
+          const int sw = (d >> 1) & 15;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (u < 2 * nkt) {
+          for (int uu = 0; uu < 2; ++uu) {
+            const int u = 2 * kt + uu;
             const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[buf][d * KC + (((4 * u + half) ^ sw) * 4)]);
             const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[buf][d * KC + (((4 * u + 2 + half) ^ sw) * 4)]);
             const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            O[dt] = mfma32x32x16(a, P[u], O[dt]);
+            O[dt] = mfma32x32x16(a, P[uu], O[dt]);
           }
         }
       }
     }
 
     if (have_next) store_chunk(buf ^ 1);
+    wait_all_memory();
     __syncthreads();
     buf ^= 1;
     cur = nxt;
@@ -360,6 +355,7 @@ bool prefill_bf16_supported(int group, int d, int block, int top_k, int seq) {
   const int mq = 4 * (32 / group);
   const size_t dyn = (size_t)(mq * top_k + ((seq - 1) / block) / 32 + 1) * 4;
   const size_t stat = (size_t)2 * 2 * KC * d * 2;
+  if ((long long)seq * 32 * d >= (1ll << 31)) return false;  // 32-bit offsets within a sequence
   return stat + dyn <= 96 * 1024;
 }
 

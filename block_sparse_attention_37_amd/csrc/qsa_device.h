@@ -29,8 +29,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even; one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Element loads that turn either storage type into float.
@@ -61,6 +67,27 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// gfx950-only builtins, kept out of the host pass of the single-source compile (the host
+// pass never runs device code, but it must still see kernel templates it can stub).
+__device__ __forceinline__ void global_to_lds16(const void* gptr, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // each lane's 16 bytes land at lds_base + 16 * lane (lds_base is wave-uniform)
+  __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void wait_all_memory() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
+}
+__device__ __forceinline__ int wave_uniform(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_readfirstlane(x);
+#else
+  return x;
+#endif
 }
 
 template <typename To, typename From>

@@ -205,6 +205,8 @@ def gpu_decode_setup(w, lens, dev, seqs=None):
     iq = torch.zeros(w.batch, w.h_idx, w.d_idx, dtype=kc.dtype, device=dev)
     keep = {}
     for b, s in S.decode_sequences(w, lens):
+        if b % 16 == 0 and w.batch >= 32:
+            say(f"  generating sequence {b}/{w.batch}")
         L = int(lens[b])
         kc[b, :L] = _t(s["k"], dev)
         vc[b, :L] = _t(s["v"], dev)
