@@ -6,23 +6,29 @@
 // grouped-query attention.
 //
 // Work decomposition
-//   * A workgroup (4 waves) owns MQ = 4 * (32 / G) consecutive query positions of one
+//   * A workgroup of NW waves owns MQ = NW * (32 / G) consecutive query positions of one
 //     KV head g; a wave owns 32 MFMA rows = (32 / G) positions x the G query heads that
 //     read KV head g.  All G heads of a position share its selection, so the rows of a
 //     wave differ in selection only per position.
 //   * The workgroup walks the UNION of the blocks its positions need (selected blocks
 //     plus the own blocks of positions whose trailing part is non-empty), kept as a
 //     bitmap in LDS and visited in ascending order.  Each block is streamed through LDS in
-//     chunks of 64 keys (K row-major, V transposed), double-buffered: the global loads of
-//     chunk u+1 are in flight while chunk u is multiplied.
+//     chunks of 64 keys.  K and V rows go global -> LDS directly (no registers) through
+//     NS stages: while chunk u is multiplied, chunks u+1 .. u+NS-1 are in flight.  Every
+//     chunk is shared by the NW waves (256 MFMA rows), which sets the flops per byte of L2
+//     traffic.
 //   * Per row visibility of a block: the lane walks its position's ascending selection
 //     list in step with the union (one compare per block), or the block is the
 //     position's own block with a non-empty trailing part; keys after p are masked
 //     (causal part of the trailing block).  A wave with no visible row skips the block.
-//   * Transposed products keep one query row per lane:  S^T = K . Q^T  (A = K from LDS,
-//     B = Q^T held in registers) and  O^T = V^T . P^T  (A = V^T from LDS, B = P^T taken
-//     straight from the S^T accumulators, the key order inside an MFMA step permuted
-//     identically on both operands).  Row max/sum need one exchange with lane ^ 32.
+//   * Transposed products keep one query row per lane:  S^T = K . Q^T  (A = K rows from
+//     LDS, B = Q^T held in registers) and  O^T = V^T . P^T  (A = V^T gathered from the
+//     row-major V tile by the LDS transpose read ds_read_b64_tr_b16, B = P^T taken straight
+//     from the S^T accumulators; the key order inside an MFMA step is permuted identically
+//     on both operands).  Row max and sum need one exchange with lane ^ 32.
+//   * Online softmax in base 2 with the scale folded into one FMA per score; the running
+//     max is raised only when it grows by more than 8 (log2 units), so rescaling the
+//     accumulators is rare and every exponent stays <= 8.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -32,7 +38,16 @@ namespace qsa {
 
 namespace {
 
-constexpr int KC = 64;  // keys per LDS chunk
+constexpr int KC = 64;   // keys per LDS chunk
+constexpr int NW = 8;    // waves per workgroup
+constexpr int NS = 4;    // LDS stages (chunks in flight + the one being used)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
 
 struct ChunkIter {
   int wi;         // bitmap word index
@@ -61,27 +76,74 @@ __device__ __forceinline__ bool advance(const uint32_t* bm, int words, int nsub,
   return next_block(bm, words, it);
 }
 
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+#endif
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies: that fence would
+// drain every outstanding LDS-direct load.  The loop waits for exactly the chunk it needs
+// (wait_vmcnt) before the barrier; the LDS it reads was filled only by those loads, and
+// the clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_barrier" ::: "memory");
+#endif
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+#else
+  (void)p;
+  return u32x2{0u, 0u};
+#endif
+}
+
+// XOR swizzles of 16-byte chunks inside a row of the LDS tiles.
+//  K: row r, chunk c -> c ^ (r mod NC16): the 32 rows an MFMA operand read touches at one
+//     chunk spread over all banks.
+//  V: the transpose read touches 8 consecutive rows x 64 bytes; rows r..r+3 must use
+//     disjoint 64-byte column groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
 }  // namespace
 
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
     float* __restrict__ lse, int seq, int h_q, int h_kv, int block, int top_k, float scale_log2,
     int ntiles, int total_wg) {
+  constexpr int NT = NW * 64;
   constexpr int PW = 32 / G;       // positions per wave
-  constexpr int MQ = 4 * PW;       // positions per workgroup
+  constexpr int MQ = NW * PW;      // positions per workgroup
   constexpr int NC16 = D / 8;      // 16-byte chunks per key row
-  constexpr int KIT = KC * NC16 / 256;  // K 16-byte items per lane per chunk
-  constexpr int VQ = KC / 4 * NC16;     // V items (4 keys x 16 bytes)
+  constexpr int RPI = 64 / NC16;   // rows one wave fills per LDS-direct instruction
+  constexpr int RPP = NW * RPI;    // rows all waves fill per instruction
+  constexpr int DPT = KC / RPP;    // instructions per wave per tile (K or V)
+  constexpr int DPC = 2 * DPT;     // per chunk (K and V)
   constexpr int NDT = D / 32;      // 32-wide d tiles of O^T
   constexpr int NKS = D / 16;      // k-steps of S^T = K . Q^T
+  static_assert(KC % RPP == 0, "tile rows");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * KC];
-  extern __shared__ __attribute__((aligned(16))) int32_t dyn[];
-  int32_t* sel_s = dyn;                                         // [MQ][top_k]
-  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn + MQ * top_k);  // union bitmap
+  // One array per stage (K rows, then V rows): every access below names its array
+  // statically, and all LDS the loop reads is statically allocated, so the compiler can
+  // tell the in-flight LDS-direct loads of other stages from the reads of this one and
+  // does not drain the load queue before each LDS read.
+  __shared__ __attribute__((aligned(16))) uint16_t KV0[2 * KC * D], KV1[2 * KC * D],
+      KV2[2 * KC * D], KV3[2 * KC * D];
+  static_assert(NS == 4, "one named array per stage");
+  __shared__ int32_t sel_s[kPrefillSelCap];    // [MQ][top_k]
+  __shared__ uint32_t bm[kPrefillMaxBlocks / 32];  // union bitmap
 
   // ---- which tile: consecutive tiles of one head land on the same XCD (L2) ----
   const int wg = blockIdx.x;
@@ -96,10 +158,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_uniform(tid >> 6);
 
   // ---- selection rows of the tile -> LDS; union bitmap ----
-  for (int e = tid; e < MQ * top_k; e += 256) {
+  for (int e = tid; e < MQ * top_k; e += NT) {
     const int pos = e / top_k;
     const int p = p0 + pos;
     int j = INT_MAX;
@@ -109,9 +171,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
     }
     sel_s[e] = j;
   }
-  for (int w = tid; w < words; w += 256) bm[w] = 0u;
+  for (int w = tid; w < words; w += NT) bm[w] = 0u;
   __syncthreads();
-  for (int e = tid; e < MQ * top_k; e += 256) {
+  for (int e = tid; e < MQ * top_k; e += NT) {
     const int j = sel_s[e];
     if (j != INT_MAX) atomicOr(&bm[j >> 5], 1u << (j & 31));
   }
@@ -137,7 +199,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   {
     const uint16_t* qp = q + (((size_t)b * seq + (valid_row ? p : 0)) * h_q + hh) * D + half * 8;
 #pragma unroll
-    for (int t = 0; t < NKS; ++t) qreg[t] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(qp + t * 16));
+    for (int t = 0; t < NKS; ++t) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qp + t * 16);
+      // opaque to the optimizer: keeps Q in registers instead of re-loading it per chunk
+      // (a re-load would also wait on the untracked K/V loads in flight)
+      keep_in_register(w);
+      qreg[t] = bitcast<bf16x8>(w);
+    }
   }
 
   int ptr = 0;
@@ -157,167 +225,158 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   const uint16_t* kbase = k + ((size_t)b * seq * h_kv + g) * D;
   const uint16_t* vbase = v + ((size_t)b * seq * h_kv + g) * D;
 
-  // K goes global -> LDS directly (no registers): wave-instruction i fills rows
-  // i*(256/NC16) + wave*RPI .. +RPI-1, lane -> (row lane/NC16, physical chunk lane%NC16),
-  // so the lane fetches the logical chunk that the XOR swizzle maps to that slot.
-  constexpr int RPI = 64 / NC16;
-  const int wave_u = wave_uniform(wave);
-  const int k_lrow = lane / NC16;
-  const int k_pc = lane % NC16;
-  // V rows vq*4+i (chunk vc) are staged in registers and written transposed.
-  const int vc = tid % NC16, vq = tid / NC16;
-  u32x4 vreg[4];
-
-  auto chunk_keys = [&](const ChunkIter& it, int& key0, int& ck) {
-    key0 = it.j * block + it.sub * KC;
-    ck = min(KC, block - it.sub * KC);
-    ck = min(ck, seq - key0);
-  };
-
-  // Rows past the chunk are clamped into the tensor; their keys are masked.
-  auto load_chunk = [&](const ChunkIter& it, int buf) {
+  // LDS-direct loads: wave instruction i fills rows i*RPP + wave*RPI .. +RPI-1; lane ->
+  // (row lane / NC16, physical chunk lane % NC16) and fetches the logical chunk that the
+  // swizzle maps to that slot.  Rows past the chunk are clamped into the tensor (masked).
+  const int d_row = lane / NC16;
+  const int d_pc = lane % NC16;
+  auto issue = [&](const ChunkIter& it, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int SI = decltype(stage_tag)::value;
+    const uint32_t kd = lds_addr(SI == 0 ? KV0 : SI == 1 ? KV1 : SI == 2 ? KV2 : KV3);
+    const uint32_t vd = kd + KC * D * 2;
     const int key0 = it.j * block + it.sub * KC;
 #pragma unroll
-    for (int i = 0; i < KIT; ++i) {
-      const int r = i * (256 / NC16) + wave_u * RPI + k_lrow;
-      const int c = k_pc ^ (r & (NC16 - 1));
-      const uint32_t row = (uint32_t)min(key0 + r, seq - 1);
-      global_to_lds16(kbase + row * kv_row + c * 8, &Ks[buf][(i * (256 / NC16) + wave_u * RPI) * D]);
-    }
-    if (tid < VQ) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t row = (uint32_t)min(key0 + vq * 4 + i, seq - 1);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + row * kv_row + vc * 8);
-      }
+    for (int i = 0; i < DPT; ++i) {
+      const int r0 = i * RPP + wave * RPI;
+      const int r = r0 + d_row;
+      const uint32_t grow = (uint32_t)min(key0 + r, seq - 1);
+      global_to_lds16_untracked(kbase + grow * kv_row + (d_pc ^ swz_k<D>(r)) * 8, kd + r0 * D * 2);
+      global_to_lds16_untracked(vbase + grow * kv_row + (d_pc ^ swz_v<D>(r)) * 8, vd + r0 * D * 2);
     }
   };
 
-  auto store_chunk = [&](int buf) {
-    if (tid < VQ) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // element pairs (2w, 2w+1) of the 4 rows -> V^T rows d = vc*8 + 2w, +1
-        const uint32_t e0lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-        const uint32_t e0hi = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-        const uint32_t e1lo = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-        const uint32_t e1hi = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-        const int d0 = vc * 8 + 2 * w, d1 = d0 + 1;
-        *reinterpret_cast<u32x2*>(&Vt[buf][d0 * KC + ((vq ^ ((d0 >> 1) & 15)) * 4)]) = u32x2{e0lo, e0hi};
-        *reinterpret_cast<u32x2*>(&Vt[buf][d1 * KC + ((vq ^ ((d1 >> 1) & 15)) * 4)]) = u32x2{e1lo, e1hi};
-      }
+  // transpose-read lane geometry (see the O^T product below)
+  const int tr_g = lane >> 4, tr_m = lane & 15;
+  const int tr_row = 4 * (tr_g >> 1) + (tr_m >> 2);      // + 16u (+8 for the upper 4 keys)
+  const int tr_d = 16 * (tr_g & 1) + 4 * (tr_m & 3);     // + 32*dt
+
+  ChunkIter it_issue{0, bm[0], -1, 0};
+  bool more_issue = next_block(bm, words, it_issue);
+  ChunkIter it = it_issue;
+  bool more = more_issue;
+  int issued = 0;
+  auto issue_next = [&](auto stage_tag) __attribute__((always_inline)) {
+    if (more_issue) {
+      issue(it_issue, stage_tag);
+      ++issued;
+      more_issue = advance(bm, words, nsub, it_issue);
     }
   };
+  issue_next(Int<0>{});
+  issue_next(Int<1>{});
+  issue_next(Int<2>{});
 
-  ChunkIter cur{0, bm[0], -1, 0};
-  bool have = next_block(bm, words, cur);
-  if (have) {
-    load_chunk(cur, 0);
-    store_chunk(0);
-  }
-  wait_all_memory();  // LDS-direct loads are counted by vmcnt
-  __syncthreads();
-  int buf = 0;
   const float ninf = -__builtin_inff();
+  int u = 0;
 
-  while (have) {
-    ChunkIter nxt = cur;
-    const bool have_next = advance(bm, words, nsub, nxt);
-    if (have_next) load_chunk(nxt, buf ^ 1);
+  // One 32-key tile of the chunk in stage Kst: S^T tile -> online softmax -> P^T -> O^T.
+  auto do_tile = [&](const uint16_t* Kst, const uint16_t* Vst, int kt, int key0, int ck,
+                     bool emask) __attribute__((always_inline)) {
+    f32x16 S;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = 0.f;
+    {
+      const int kr = kt * 32 + row;
+#pragma unroll
+      for (int t = 0; t < NKS; ++t) {
+        const int c = t * 2 + half;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kst[kr * D + ((c ^ swz_k<D>(kr)) * 8)]);
+        S = mfma32x32x16(a, qreg[t], S);
+      }
+    }
+    if (emask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (kr >= ck || key0 + kr > p) S[r] = ninf;
+      }
+    }
+    float mx = ninf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_cand = vis ? fmaxf(m_run, mx * scale_log2) : m_run;
+    const bool need = m_cand > m_run + 8.0f;
+    if (__ballot(need) != 0ull) {
+      const float m_new = need ? m_cand : m_run;
+      // lanes that keep their max (possibly still -inf) keep their state exactly
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+    }
+    const float nb = (vis && m_run != ninf) ? -m_run : ninf;
+    float psum = 0.f;
+    bf16x8 P[2];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      u32x4 w;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * uu + 2 * jj], scale_log2, nb));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * uu + 2 * jj + 1], scale_log2, nb));
+        psum += e0 + e1;
+        w[jj] = pack_bf16x2(e0, e1);
+      }
+      P[uu] = bitcast<bf16x8>(w);
+    }
+    l_run += psum;
+    // A operand of step u: V at d = 32*dt + (lane % 32), keys 16u + 4*(lane/32) + {0..3}
+    // and 16u + 8 + 4*(lane/32) + {0..3}; each half is one transpose read in which the
+    // lane supplies row 16u + tr_row (+8), columns 32*dt + tr_d .. +3.
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int r_lo = 16 * (2 * kt + uu) + tr_row;
+      const int r_hi = r_lo + 8;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int dcol = 32 * dt + tr_d;
+        const u32x2 lo = lds_read_tr16(&Vst[r_lo * D + (((dcol >> 3) ^ swz_v<D>(r_lo)) * 8) + (dcol & 7)]);
+        const u32x2 hi = lds_read_tr16(&Vst[r_hi * D + (((dcol >> 3) ^ swz_v<D>(r_hi)) * 8) + (dcol & 7)]);
+        const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        O[dt] = mfma32x32x16(a, P[uu], O[dt]);
+      }
+    }
+  };
 
-    if (cur.sub == 0) {
-      const bool hit = (cur_sel == cur.j);
+  // One chunk per call, stage S fixed at compile time.
+  auto step = [&](auto stage_tag) __attribute__((always_inline)) -> bool {
+    constexpr int S = decltype(stage_tag)::value;
+    const uint16_t* Kst = S == 0 ? KV0 : S == 1 ? KV1 : S == 2 ? KV2 : KV3;
+    const uint16_t* Vst = Kst + KC * D;
+    if (!more) return false;
+    // chunk u must have landed; the (at most NS-2) chunks after it may stay in flight
+    const int after = issued - u - 1;
+    if (after >= 2) wait_vmcnt<2 * DPC>();
+    else if (after == 1) wait_vmcnt<DPC>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    issue_next(Int<(S + NS - 1) % NS>{});  // refills the stage chunk u-1 used
+
+    if (it.sub == 0) {
+      const bool hit = (cur_sel == it.j);
       if (hit) {
         ++ptr;
         cur_sel = (ptr < top_k) ? sel_s[pos * top_k + ptr] : INT_MAX;
       }
-      vis = valid_row && (hit || cur.j == own_block);
+      vis = valid_row && (hit || it.j == own_block);
     }
-
     if (__ballot(vis) != 0ull) {
-      int key0, ck;
-      chunk_keys(cur, key0, ck);
+      const int key0 = it.j * block + it.sub * KC;
+      const int ck = min(min(KC, block - it.sub * KC), seq - key0);
       const bool emask = ck < KC || key0 + KC - 1 > p0;  // keys past the chunk or after p
-      // one 32-key tile at a time: S^T tile -> online softmax -> P^T -> O^T update
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        if (kt == 1 && ck <= 32) break;
-        f32x16 S;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = 0.f;
-        {
-          const int kr = kt * 32 + row;
-#pragma unroll
-          for (int t = 0; t < NKS; ++t) {
-            const int c = t * 2 + half;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[buf][kr * D + ((c ^ (kr & (NC16 - 1))) * 8)]);
-            S = mfma32x32x16(a, qreg[t], S);
-          }
-        }
-        if (emask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kr = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (kr >= ck || key0 + kr > p) S[r] = ninf;
-          }
-        }
-        float mx = ninf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // the running max moves only when it grows by more than 8 (log2 units): rare
-        // rescales, and every exponent below stays <= 8
-        const float m_cand = vis ? fmaxf(m_run, mx * scale_log2) : m_run;
-        const bool need = m_cand > m_run + 8.0f;
-        if (__ballot(need) != 0ull) {
-          const float m_new = need ? m_cand : m_run;
-          // lanes that keep their max (possibly still -inf) keep their state exactly
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-          m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-        }
-        const float nb = (vis && m_run != ninf) ? -m_run : ninf;
-        float psum = 0.f;
-        bf16x8 P[2];
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-          u32x4 w;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * uu + 2 * jj], scale_log2, nb));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * uu + 2 * jj + 1], scale_log2, nb));
-            psum += e0 + e1;
-            w[jj] = pack_bf16x2(e0, e1);
-          }
-          P[uu] = bitcast<bf16x8>(w);
-        }
-        l_run += psum;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int d = dt * 32 + row;
-          const int sw = (d >> 1) & 15;
-#pragma unroll
-          for (int uu = 0; uu < 2; ++uu) {
-            const int u = 2 * kt + uu;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[buf][d * KC + (((4 * u + half) ^ sw) * 4)]);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[buf][d * KC + (((4 * u + 2 + half) ^ sw) * 4)]);
-            const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            O[dt] = mfma32x32x16(a, P[uu], O[dt]);
-          }
-        }
-      }
+      do_tile(Kst, Vst, 0, key0, ck, emask);
+      if (ck > 32) do_tile(Kst, Vst, 1, key0, ck, emask);
     }
 
-    if (have_next) store_chunk(buf ^ 1);
-    wait_all_memory();
-    __syncthreads();
-    buf ^= 1;
-    cur = nxt;
-    have = have_next;
+    more = advance(bm, words, nsub, it);
+    ++u;
+    return more;
+  };
+  while (step(Int<0>{}) && step(Int<1>{}) && step(Int<2>{}) && step(Int<3>{})) {
   }
 
   // ---- epilogue ----
@@ -341,34 +400,24 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(
   }
 }
 
-template <int D, int G>
-static size_t prefill_dyn_lds(int seq, int block, int top_k) {
-  constexpr int MQ = 4 * (32 / G);
-  const int words = ((seq - 1) / block) / 32 + 1;
-  return (size_t)(MQ * top_k + words) * 4;
-}
-
 bool prefill_bf16_supported(int group, int d, int block, int top_k, int seq) {
   if (d != 64 && d != 128) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16 && group != 32) return false;
   if (block < 1 || block > 1024 || top_k < 1 || top_k > kMaxTopK) return false;
-  const int mq = 4 * (32 / group);
-  const size_t dyn = (size_t)(mq * top_k + ((seq - 1) / block) / 32 + 1) * 4;
-  const size_t stat = (size_t)2 * 2 * KC * d * 2;
   if ((long long)seq * 32 * d >= (1ll << 31)) return false;  // 32-bit offsets within a sequence
-  return stat + dyn <= 96 * 1024;
+  if ((long long)NW * (32 / group) * top_k > kPrefillSelCap) return false;
+  return (seq + block - 1) / block <= kPrefillMaxBlocks;
 }
 
 template <int D, int G>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const int32_t* sel,
                                    void* out, float* lse, int batch, int seq, int h_q, int h_kv,
                                    int block, int top_k, float sm_scale, hipStream_t stream) {
-  constexpr int MQ = 4 * (32 / G);
+  constexpr int MQ = NW * (32 / G);
   const int ntiles = (seq + MQ - 1) / MQ;
   const long long total = (long long)ntiles * h_kv * batch;
   if (total > INT_MAX) return hipErrorInvalidValue;
-  const size_t dyn = prefill_dyn_lds<D, G>(seq, block, top_k);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3((unsigned)total), dim3(256), dyn, stream,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3((unsigned)total), dim3(NW * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse, seq,
                      h_q, h_kv, block, top_k, sm_scale * kLog2e, ntiles, (int)total);

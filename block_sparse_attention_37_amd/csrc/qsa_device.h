@@ -77,6 +77,33 @@ __device__ __forceinline__ void global_to_lds16(const void* gptr, void* lds_base
   __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
 #endif
 }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Same 16-byte global -> LDS load, issued so that the compiler does not track it.  The
+// compiler cannot tell LDS-direct loads into one buffer from LDS reads of another and
+// would drain every such load before each LDS read; kernels using this form count the
+// loads themselves and wait for them (s_waitcnt vmcnt) before the barrier that publishes
+// the buffer.  No register is written by the instruction, and M0 / the address are read
+// when it issues (M0 gets its previous value back right after).
+__device__ __forceinline__ void global_to_lds16_untracked(const void* gptr, uint32_t lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t saved;  // M0 is reserved by the compiler: restore it after use
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gptr));
+#else
+  (void)gptr;
+  (void)lds_base;
+#endif
+}
 __device__ __forceinline__ void wait_all_memory() {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_s_waitcnt(0);
@@ -87,6 +114,13 @@ __device__ __forceinline__ int wave_uniform(int x) {
   return __builtin_amdgcn_readfirstlane(x);
 #else
   return x;
+#endif
+}
+
+// Makes a value opaque to the optimizer (no rematerialization, no sinking of its load).
+__device__ __forceinline__ void keep_in_register(u32x4& w) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(w));
 #endif
 }
 

@@ -21,6 +21,10 @@ hipError_t launch_index_topk(const void* iq, const float* cmp, const int32_t* kv
                              hipStream_t stream);
 
 // bf16 prefill on matrix cores.  Returns hipErrorInvalidValue for shapes it is not built for.
+// A workgroup keeps the selection rows of its query positions (positions x top_k entries)
+// and a bitmap of the blocks it visits in LDS.
+constexpr int kPrefillSelCap = 4096;
+constexpr int kPrefillMaxBlocks = 4096;
 bool prefill_bf16_supported(int group, int d, int block, int top_k, int seq);
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, const int32_t* sel,
                                void* out, float* lse, int batch, int seq, int h_q, int h_kv,
