@@ -56,10 +56,12 @@ struct ChunkIter {
   int sub;        // 64-key sub-chunk inside the block
 };
 
+// The bitmap is the same for every lane: its words are made wave-uniform so the walk runs
+// on the scalar unit.
 __device__ __forceinline__ bool next_block(const uint32_t* bm, int words, ChunkIter& it) {
   while (it.bits == 0u) {
     if (++it.wi >= words) return false;
-    it.bits = bm[it.wi];
+    it.bits = (uint32_t)wave_uniform((int)bm[it.wi]);
   }
   const int t = __builtin_ctz(it.bits);
   it.bits &= it.bits - 1u;
@@ -95,6 +97,36 @@ __device__ __forceinline__ void barrier_no_fence() {
 #endif
 }
 
+// Instruction-order hints for the scheduler (no effect on results): mask selects the
+// instruction class (0x8 MFMA, 0x100 LDS read), n how many of them come next.
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+#endif
+}
+constexpr int kSchedMfma = 0x8;
+constexpr int kSchedDsRead = 0x100;
+
+// max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap leaves each lane with
+// its own value and its partner's, in some order, which max and sum do not care about.
+__device__ __forceinline__ float pair_max(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+#else
+  return x;
+#endif
+}
+__device__ __forceinline__ float pair_sum(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+#else
+  return x;
+#endif
+}
+
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -105,15 +137,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 #endif
 }
 
-// XOR swizzles of 16-byte chunks inside a row of the LDS tiles.
-//  K: row r, chunk c -> c ^ (r mod NC16): the 32 rows an MFMA operand read touches at one
-//     chunk spread over all banks.
-//  V: the transpose read touches 8 consecutive rows x 64 bytes; rows r..r+3 must use
-//     disjoint 64-byte column groups.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) { return r & (D / 8 - 1); }
-template <int D>
-__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+// LDS layout of one stage (byte offsets), chosen so that every operand read of a lane is
+// one base register plus an immediate and every read is free of bank conflicts:
+//  K: D/16 slabs of 16 columns (one per k-step t of S^T = K . Q^T), slab t at t * 2048;
+//     row r at r * 32, its two 16-byte units swapped when bit 2 of r is set (8 lanes of a
+//     ds_read_b128 phase then cover all 32 banks).
+//  V: D/32 slabs of 32 columns (one per 32-wide d tile of O^T), after the K slabs, slab dt at
+//     dt * 4096; row r at r * 64, its two 32-byte halves swapped when bit 1 of r is set (the
+//     4 rows x 32 bytes of a transpose-read phase then cover all banks).
+__device__ __forceinline__ int k_unit_swap(int r) { return (r >> 2) & 1; }
+__device__ __forceinline__ int v_half_swap(int r) { return (r >> 1) & 1; }
 
 }  // namespace
 
@@ -126,30 +159,29 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   constexpr int NT = NW * 64;
   constexpr int PW = 32 / G;       // positions per wave
   constexpr int MQ = NW * PW;      // positions per workgroup
-  constexpr int NC16 = D / 8;      // 16-byte chunks per key row
-  constexpr int RPI = 64 / NC16;   // rows one wave fills per LDS-direct instruction
-  constexpr int RPP = NW * RPI;    // rows all waves fill per instruction
-  constexpr int DPT = KC / RPP;    // instructions per wave per tile (K or V)
-  constexpr int DPC = 2 * DPT;     // per chunk (K and V)
+  constexpr int KI = 2 * (D / 16) / NW;  // LDS-direct instructions per wave per K chunk
+  constexpr int VI = 4 * (D / 32) / NW;  // ... per V chunk
+  constexpr int DPC = KI + VI;           // per chunk
+  static_assert(KI * NW == 2 * (D / 16) && VI * NW == 4 * (D / 32), "load split");
+  static_assert(KC == 64, "slab layout assumes 64-key chunks");
   constexpr int NDT = D / 32;      // 32-wide d tiles of O^T
   constexpr int NKS = D / 16;      // k-steps of S^T = K . Q^T
-  static_assert(KC % RPP == 0, "tile rows");
 
-  // One array per stage (K rows, then V rows): every access below names its array
-  // statically, and all LDS the loop reads is statically allocated, so the compiler can
-  // tell the in-flight LDS-direct loads of other stages from the reads of this one and
-  // does not drain the load queue before each LDS read.
-  __shared__ __attribute__((aligned(16))) uint16_t KV0[2 * KC * D], KV1[2 * KC * D],
-      KV2[2 * KC * D], KV3[2 * KC * D];
-  static_assert(NS == 4, "one named array per stage");
+  // NS stages of (K chunk, V chunk).  The LDS-direct loads are issued outside the
+  // compiler's view (global_to_lds16_untracked), so a stage may be picked at run time
+  // without the compiler draining the load queue before LDS reads.
+  constexpr int TILE = KC * D;     // elements of one K (or V) chunk
+  __shared__ __attribute__((aligned(16))) uint16_t ring[NS * 2 * TILE];
   __shared__ int32_t sel_s[kPrefillSelCap];    // [MQ][top_k]
   __shared__ uint32_t bm[kPrefillMaxBlocks / 32];  // union bitmap
 
-  // ---- which tile: consecutive tiles of one head land on the same XCD (L2) ----
+  // ---- which tile: consecutive tiles of one head land on the same XCD (L2); tiles are
+  // dispatched from the end of the sequence (most candidate blocks) backwards, so the last
+  // workgroups to start are the cheap ones near the beginning ----
   const int wg = blockIdx.x;
   const int per = total_wg / 8;
   const int logical = (wg < per * 8) ? (wg % 8) * per + wg / 8 : wg;
-  const int tile = logical % ntiles;
+  const int tile = ntiles - 1 - logical % ntiles;
   const int g = (logical / ntiles) % h_kv;
   const int b = logical / (ntiles * h_kv);
   const int p0 = tile * MQ;
@@ -208,10 +240,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     }
   }
 
-  int ptr = 0;
-  int cur_sel = valid_row ? sel_s[pos * top_k] : INT_MAX;
-  bool vis = false;
-
   float m_run = -__builtin_inff();
   float l_run = 0.f;
   f32x16 O[NDT];
@@ -225,23 +253,45 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const uint16_t* kbase = k + ((size_t)b * seq * h_kv + g) * D;
   const uint16_t* vbase = v + ((size_t)b * seq * h_kv + g) * D;
 
-  // LDS-direct loads: wave instruction i fills rows i*RPP + wave*RPI .. +RPI-1; lane ->
-  // (row lane / NC16, physical chunk lane % NC16) and fetches the logical chunk that the
-  // swizzle maps to that slot.  Rows past the chunk are clamped into the tensor (masked).
-  const int d_row = lane / NC16;
-  const int d_pc = lane % NC16;
-  auto issue = [&](const ChunkIter& it, auto stage_tag) __attribute__((always_inline)) {
-    constexpr int SI = decltype(stage_tag)::value;
-    const uint32_t kd = lds_addr(SI == 0 ? KV0 : SI == 1 ? KV1 : SI == 2 ? KV2 : KV3);
-    const uint32_t vd = kd + KC * D * 2;
-    const int key0 = it.j * block + it.sub * KC;
+  // number of chunks the workgroup walks
+  int nblk = 0;
+  for (int w = 0; w < words; ++w) nblk += __builtin_popcount((uint32_t)wave_uniform((int)bm[w]));
+  const int n = wave_uniform(nblk * nsub);
+
+  // LDS-direct loads: each instruction fills 1 KB of a stage (64 lanes x 16 bytes).
+  //  K: 2 per slab; piece part of slab t holds rows 32*part .. +31, lane -> (row lane / 2,
+  //     physical unit lane % 2) and fetches the logical unit the swap maps there.
+  //  V: 4 per slab; piece part of slab dt holds rows 16*part .. +15, lane -> (row lane / 4,
+  //     physical unit lane % 4).
+  // Wave w issues K pieces w*KI .. +KI-1 and V pieces w*VI .. +VI-1.  Rows past the chunk
+  // are clamped into the tensor (their keys are masked).
+  const uint32_t ring_lds = lds_addr(ring);
+  ChunkIter it_load{0, (uint32_t)wave_uniform((int)bm[0]), -1, 0};
+  next_block(bm, words, it_load);
+  int issued = 0;
+  // chunk `issued` -> stage issued % NS
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if (issued < n) {
+      const int key0 = it_load.j * block + it_load.sub * KC;
+      const uint32_t st0 = ring_lds + (uint32_t)(issued % NS) * (2 * TILE * 2);
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-      const int r0 = i * RPP + wave * RPI;
-      const int r = r0 + d_row;
-      const uint32_t grow = (uint32_t)min(key0 + r, seq - 1);
-      global_to_lds16_untracked(kbase + grow * kv_row + (d_pc ^ swz_k<D>(r)) * 8, kd + r0 * D * 2);
-      global_to_lds16_untracked(vbase + grow * kv_row + (d_pc ^ swz_v<D>(r)) * 8, vd + r0 * D * 2);
+      for (int i = 0; i < KI; ++i) {
+        const int id = wave * KI + i, t = id >> 1, part = id & 1;
+        const int r = 32 * part + (lane >> 1);
+        const int col = 16 * t + 8 * ((lane & 1) ^ k_unit_swap(r));
+        const uint32_t grow = (uint32_t)min(key0 + r, seq - 1);
+        global_to_lds16_untracked(kbase + grow * kv_row + col, st0 + t * 2048 + part * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < VI; ++i) {
+        const int id = wave * VI + i, dt = id >> 2, part = id & 3;
+        const int r = 16 * part + (lane >> 2);
+        const int col = 32 * dt + 8 * ((lane & 3) ^ (2 * v_half_swap(r)));
+        const uint32_t grow = (uint32_t)min(key0 + r, seq - 1);
+        global_to_lds16_untracked(vbase + grow * kv_row + col, st0 + TILE * 2 + dt * 4096 + part * 1024);
+      }
+      ++issued;
+      if (issued < n) advance(bm, words, nsub, it_load);
     }
   };
 
@@ -249,52 +299,95 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int tr_g = lane >> 4, tr_m = lane & 15;
   const int tr_row = 4 * (tr_g >> 1) + (tr_m >> 2);      // + 16u (+8 for the upper 4 keys)
   const int tr_d = 16 * (tr_g & 1) + 4 * (tr_m & 3);     // + 32*dt
-
-  ChunkIter it_issue{0, bm[0], -1, 0};
-  bool more_issue = next_block(bm, words, it_issue);
-  ChunkIter it = it_issue;
-  bool more = more_issue;
-  int issued = 0;
-  auto issue_next = [&](auto stage_tag) __attribute__((always_inline)) {
-    if (more_issue) {
-      issue(it_issue, stage_tag);
-      ++issued;
-      more_issue = advance(bm, words, nsub, it_issue);
-    }
-  };
-  issue_next(Int<0>{});
-  issue_next(Int<1>{});
-  issue_next(Int<2>{});
+  // per-lane byte offsets of the operand reads inside a stage
+  const int k_lane = row * 32 + 16 * (half ^ k_unit_swap(row));
+  const int v_lane = TILE * 2 + tr_row * 64 + ((tr_d * 2) ^ (32 * v_half_swap(tr_row)));
 
   const float ninf = -__builtin_inff();
-  int u = 0;
 
-  // One 32-key tile of the chunk in stage Kst: S^T tile -> online softmax -> P^T -> O^T.
-  auto do_tile = [&](const uint16_t* Kst, const uint16_t* Vst, int kt, int key0, int ck,
-                     bool emask) __attribute__((always_inline)) {
-    f32x16 S;
+  // Ping-pong: waves 0 .. NW/2-1 (group A) and NW/2 .. NW-1 (group B) hold one wave per
+  // SIMD each and run the same sequence of phases half a step apart:
+  //   MFMA phase of chunk c:  S(c) = K(c) . Q^T  and  O += V(c-1)^T . P(c-1)
+  //   VALU phase of chunk c:  mask, row max, lazy rescale, P(c) = exp2(...), row sums
+  // Between two workgroup barriers one group runs an MFMA phase while the other runs a
+  // VALU phase, so each SIMD has matrix work from one wave and vector work from the other.
+  // S and P are single buffers: each phase consumes what the previous one of the same
+  // wave produced.
+  f32x16 S[2];
+  bf16x8 P[4];
+
+  auto mfma_phase = [&](int c, bool do_s, bool do_pv) __attribute__((always_inline)) {
+    const char* Ks = reinterpret_cast<const char*>(ring + (c % NS) * (2 * TILE));
+    const char* Vp = reinterpret_cast<const char*>(ring + ((c + NS - 1) % NS) * (2 * TILE));
+    if (do_s) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = 0.f;
-    {
-      const int kr = kt * 32 + row;
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int t = 0; t < NKS; ++t) {
-        const int c = t * 2 + half;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kst[kr * D + ((c ^ swz_k<D>(kr)) * 8)]);
-        S = mfma32x32x16(a, qreg[t], S);
+        for (int r = 0; r < 16; ++r) S[kt][r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NKS; ++t) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + k_lane + t * 2048 + kt * 1024);
+          S[kt] = mfma32x32x16(a, qreg[t], S[kt]);
+        }
       }
-    }
-    if (emask) {
+      // operand reads run two MFMAs ahead
+      sched_group<kSchedDsRead, 2>();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (kr >= ck || key0 + kr > p) S[r] = ninf;
+      for (int i = 0; i < 2 * NKS - 2; ++i) {
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsRead, 1>();
       }
+      sched_group<kSchedMfma, 2>();
     }
-    float mx = ninf;
+    if (do_pv) {
+      // A operand of 16-key step st: V at d = 32*dt + (lane % 32), keys 16st + 4*half +
+      // {0..3} and 16st + 8 + 4*half + {0..3}; each half is one transpose read in which the
+      // lane supplies row 16st + tr_row (+8), columns 32*dt + tr_d .. +3.
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const char* vb = Vp + v_lane + dt * 4096 + st * 1024;
+          const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vb));
+          const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vb + 512));
+          const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          O[dt] = mfma32x32x16(a, P[st], O[dt]);
+        }
+      }
+      // two transpose reads per MFMA, running two MFMAs ahead
+      sched_group<kSchedDsRead, 4>();
+#pragma unroll
+      for (int i = 0; i < 4 * NDT - 2; ++i) {
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsRead, 2>();
+      }
+      sched_group<kSchedMfma, 2>();
+    }
+  };
+
+  // S holds the scores of a whole 64-key chunk; keys past the chunk (clamped rows, finite)
+  // and keys after the row's position are masked.  Key 32*kt + 8*(r/4) + 4*half + r%4.
+  auto valu_phase = [&](bool vis, int key0, int ck) __attribute__((always_inline)) {
+    if (ck < KC || key0 + KC - 1 > p0) {
+      const int lim = min(ck - 1, p - key0) - 4 * half;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) S[kt][r] = ninf;
+    }
+    // row max: a tree over the lane's 32 scores (short dependency chains), then the other
+    // half of the row on lane ^ 32
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = fmaxf(S[0][r], S[1][r]);
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) t[r] = fmaxf(t[r], t[r + w]);
+    const float mx = pair_max(t[0]);
+    // the running max moves only when it grows by more than 8 (log2 units): rare rescales,
+    // and every exponent stays <= 8
     const float m_cand = vis ? fmaxf(m_run, mx * scale_log2) : m_run;
     const bool need = m_cand > m_run + 8.0f;
     if (__ballot(need) != 0ull) {
@@ -309,78 +402,98 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
     }
     const float nb = (vis && m_run != ninf) ? -m_run : ninf;
-    float psum = 0.f;
-    bf16x8 P[2];
+    // probabilities: all exponent arguments first, then the exponentials, so that
+    // independent instructions separate each producer from its consumer
+    float e[32];
 #pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      u32x4 w;
+    for (int i = 0; i < 32; ++i) e[i] = __builtin_fmaf(S[i >> 4][i & 15], scale_log2, nb);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * uu + 2 * jj], scale_log2, nb));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * uu + 2 * jj + 1], scale_log2, nb));
-        psum += e0 + e1;
-        w[jj] = pack_bf16x2(e0, e1);
-      }
-      P[uu] = bitcast<bf16x8>(w);
+    for (int i = 0; i < 32; ++i) e[i] = __builtin_amdgcn_exp2f(e[i]);
+    // B operand of 16-key step st: S registers 8*(st & 1) .. +7 of key tile st / 2
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int i0 = 16 * (st >> 1) + 8 * (st & 1);
+      P[st] = bitcast<bf16x8>(u32x4{pack_bf16x2(e[i0], e[i0 + 1]), pack_bf16x2(e[i0 + 2], e[i0 + 3]),
+                                    pack_bf16x2(e[i0 + 4], e[i0 + 5]), pack_bf16x2(e[i0 + 6], e[i0 + 7])});
     }
-    l_run += psum;
-    // A operand of step u: V at d = 32*dt + (lane % 32), keys 16u + 4*(lane/32) + {0..3}
-    // and 16u + 8 + 4*(lane/32) + {0..3}; each half is one transpose read in which the
-    // lane supplies row 16u + tr_row (+8), columns 32*dt + tr_d .. +3.
 #pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      const int r_lo = 16 * (2 * kt + uu) + tr_row;
-      const int r_hi = r_lo + 8;
+    for (int w = 16; w >= 1; w >>= 1)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int dcol = 32 * dt + tr_d;
-        const u32x2 lo = lds_read_tr16(&Vst[r_lo * D + (((dcol >> 3) ^ swz_v<D>(r_lo)) * 8) + (dcol & 7)]);
-        const u32x2 hi = lds_read_tr16(&Vst[r_hi * D + (((dcol >> 3) ^ swz_v<D>(r_hi)) * 8) + (dcol & 7)]);
-        const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        O[dt] = mfma32x32x16(a, P[uu], O[dt]);
-      }
-    }
+      for (int i = 0; i < w; ++i) e[i] += e[i + w];
+    l_run += e[0];
   };
 
-  // One chunk per call, stage S fixed at compile time.
-  auto step = [&](auto stage_tag) __attribute__((always_inline)) -> bool {
-    constexpr int S = decltype(stage_tag)::value;
-    const uint16_t* Kst = S == 0 ? KV0 : S == 1 ? KV1 : S == 2 ? KV2 : KV3;
-    const uint16_t* Vst = Kst + KC * D;
-    if (!more) return false;
-    // chunk u must have landed; the (at most NS-2) chunks after it may stay in flight
-    const int after = issued - u - 1;
-    if (after >= 2) wait_vmcnt<2 * DPC>();
-    else if (after == 1) wait_vmcnt<DPC>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();
-    issue_next(Int<(S + NS - 1) % NS>{});  // refills the stage chunk u-1 used
-
-    if (it.sub == 0) {
-      const bool hit = (cur_sel == it.j);
+  // ---- selection walk: visibility of each chunk for this lane's row ----
+  ChunkIter it_vis{0, (uint32_t)wave_uniform((int)bm[0]), -1, 0};
+  int ptr = 0;
+  int cur_sel = valid_row ? sel_s[pos * top_k] : INT_MAX;
+  bool vis = false;
+  auto visit = [&](bool first) __attribute__((always_inline)) {
+    if (first) next_block(bm, words, it_vis);
+    else advance(bm, words, nsub, it_vis);
+    if (it_vis.sub == 0) {
+      const bool hit = (cur_sel == it_vis.j);
       if (hit) {
         ++ptr;
         cur_sel = (ptr < top_k) ? sel_s[pos * top_k + ptr] : INT_MAX;
       }
-      vis = valid_row && (hit || it.j == own_block);
+      vis = valid_row && (hit || it_vis.j == own_block);
     }
-    if (__ballot(vis) != 0ull) {
-      const int key0 = it.j * block + it.sub * KC;
-      const int ck = min(min(KC, block - it.sub * KC), seq - key0);
-      const bool emask = ck < KC || key0 + KC - 1 > p0;  // keys past the chunk or after p
-      do_tile(Kst, Vst, 0, key0, ck, emask);
-      if (ck > 32) do_tile(Kst, Vst, 1, key0, ck, emask);
-    }
-
-    more = advance(bm, words, nsub, it);
-    ++u;
-    return more;
   };
-  while (step(Int<0>{}) && step(Int<1>{}) && step(Int<2>{}) && step(Int<3>{})) {
+
+  // Chunk u: both groups meet barrier 1 (after chunk u has landed) and barrier 2.
+  //   group A:  barrier 1, MFMA phase u, barrier 2, VALU phase u
+  //   group B:  barrier 1, VALU phase u-1, barrier 2, MFMA phase u
+  // followed by the O product of chunk n-1.  The groups run separate loops with the same
+  // barriers, so each loop is straight-line code for the register allocator.
+  bool vis_prev = false, any_prev = false;
+  int key0_prev = 0, ck_prev = 0;
+  auto chunk_begin = [&](int u, bool& vis_u, bool& any_u, int& key0_u, int& ck_u)
+      __attribute__((always_inline)) {
+    // chunk u must have landed; chunk u+1 may stay in flight
+    if (issued > u + 1) wait_vmcnt<DPC>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    // every wave is past chunk u-2 (its last reader, the O product of group B, ended
+    // before this barrier): its stage takes chunk u+2
+    issue_next();
+    visit(u == 0);
+    vis_u = vis;
+    key0_u = it_vis.j * block + it_vis.sub * KC;
+    ck_u = min(min(KC, block - it_vis.sub * KC), seq - key0_u);
+    any_u = __ballot(vis) != 0ull;
+  };
+  issue_next();
+  issue_next();
+  if (wave < NW / 2) {
+    for (int u = 0; u < n; ++u) {
+      bool vis_u, any_u;
+      int key0_u, ck_u;
+      chunk_begin(u, vis_u, any_u, key0_u, ck_u);
+      mfma_phase(u, any_u, any_prev);
+      barrier_no_fence();
+      if (any_u) valu_phase(vis_u, key0_u, ck_u);
+      any_prev = any_u;
+    }
+  } else {
+    for (int u = 0; u < n; ++u) {
+      bool vis_u, any_u;
+      int key0_u, ck_u;
+      chunk_begin(u, vis_u, any_u, key0_u, ck_u);
+      if (any_prev) valu_phase(vis_prev, key0_prev, ck_prev);
+      barrier_no_fence();
+      mfma_phase(u, any_u, any_prev);
+      vis_prev = vis_u;
+      any_prev = any_u;
+      key0_prev = key0_u;
+      ck_prev = ck_u;
+    }
+    if (any_prev) valu_phase(vis_prev, key0_prev, ck_prev);
   }
+  if (any_prev) mfma_phase(n, false, true);
 
   // ---- epilogue ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (valid_row) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = out + (((size_t)b * seq + p) * h_q + hh) * D;
