@@ -3,6 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--graph | --no-graph] [--no-cpu-baseline]
+    python bench.py --calibrate-copy MIB
+
 
 A step is one pass of the whole QSA path over one batch of synthetic input:
   prefill workloads: key-block compression -> indexer scores + top-k selection
@@ -16,9 +18,17 @@ tokens/s of the whole step (prefill: batch*seq tokens, decode: batch tokens).
 ``roofline`` describes the dominant kernel (the attention kernel): algorithmic
 flops (prefill, bf16 matrix cores) or algorithmic bytes (decode, HBM) per launch
 divided by its average launch time, measured with events recorded on the stream
-the kernels run on, around every attention launch of the timed steps.
+the kernels run on around `steps` back-to-back attention calls that follow the
+timed steps.  ``traffic`` is the HBM byte count per launch from the committed
+profiler counter summary of the workload (null when the kernel sources changed
+since it was taken).
 ``cpu_baseline`` times the fp64 oracle (single-threaded BLAS) on a bounded
 sample of the same workload.
+
+``--calibrate-copy MIB`` runs only a plain device copy of MIB MiB (one
+elementwise kernel that reads and writes MIB MiB, five launches): the byte
+counters of the profiler (FETCH_SIZE, WRITE_SIZE) read on it give the scale
+factors that turn the counters of the attention kernels into bytes.
 """
 from __future__ import annotations
 
@@ -53,7 +63,27 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run only a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> int:
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * 2**20
+    x = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        torch.mul(x, 1.0, out=y)  # one elementwise kernel: reads n bytes, writes n bytes
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"calibration": "device copy (elementwise multiply by 1.0)",
+                      "bytes_read_per_launch": n, "bytes_written_per_launch": n, "launches": 5,
+                      "ms_per_launch": round(dt * 1e3, 4)}), flush=True)
+    return 0
 
 
 # ---------------------------------------------------------------------------
@@ -196,6 +226,8 @@ def main():
         print(json.dumps({"error": "this QSA build runs on exactly one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is described in DESIGN.md, not built)"}))
         return 2
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy)
     import torch
     from block_sparse_attention_37_amd import synth as S
     w = S.WORKLOADS[args.workload]
@@ -237,21 +269,37 @@ def main():
         run_attention()
     torch.cuda.synchronize()
 
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
         run_index()
-        ev_a[i].record(stream)
         run_attention()
-        ev_b[i].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    att_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
     ms_per_step = total_ms / steps
+
+    # Launch duration of the attention call for the roofline: `steps` back-to-back calls
+    # between two events on the stream the kernels run on (launch gaps amortised, so the
+    # figure compares with a profiler's per-kernel average duration).
+    if args.graph:
+        g_rep = torch.cuda.CUDAGraph()  # the `steps` calls as one graph: no per-replay gaps
+        with torch.cuda.graph(g_rep):
+            for i in range(steps):
+                plan.run_attention()
+        torch.cuda.synchronize()
+        run_rep = g_rep.replay
+    else:
+        def run_rep():
+            for i in range(steps):
+                plan.run_attention()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    run_rep()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    att_ms = a0.elapsed_time(a1) / steps
     value = tokens / (ms_per_step / 1e3)
 
     if w.kind == "prefill":
@@ -265,7 +313,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = load_traffic(w.name)
-    roof["kernel"] = "qsa::prefill_bf16_kernel" if w.kind == "prefill" else "qsa::decode_bf16_kernel"
+    # the attention call: one kernel for prefill; split kernel + merge kernel for decode
+    roof["kernel"] = ("qsa::prefill_bf16_kernel" if w.kind == "prefill"
+                      else "qsa::decode_bf16_kernel + qsa::decode_merge_kernel")
     roof["algorithmic_per_launch"] = work
     roof["kernel_ms"] = round(att_ms, 5)
 
