@@ -251,30 +251,26 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     if args.graph:
-        # two graphs per step so that events can bracket the attention launch
-        g_idx, g_att = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        # one graph per step: index (+ compression for prefill), then attention
+        g_step = torch.cuda.CUDAGraph()
         plan.run()  # warm the launch path before capture
         torch.cuda.synchronize()
-        with torch.cuda.graph(g_idx):
-            plan.run_index()
-        with torch.cuda.graph(g_att):
-            plan.run_attention()
+        with torch.cuda.graph(g_step):
+            plan.run()
         torch.cuda.synchronize()
-        run_index, run_attention = g_idx.replay, g_att.replay
+        run_step = g_step.replay
     else:
-        run_index, run_attention = plan.run_index, plan.run_attention
+        run_step = plan.run
 
     for _ in range(warmup):
-        run_index()
-        run_attention()
+        run_step()
     torch.cuda.synchronize()
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
-        run_index()
-        run_attention()
+        run_step()
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)

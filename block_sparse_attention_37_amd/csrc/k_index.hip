@@ -142,8 +142,11 @@ static hipError_t launch_index_nr(const void* iq, const float* cmp, const int32_
                                   int32_t* sel, float* sel_scores, int batch, int n_q, int h_idx,
                                   int d_idx, int max_blocks, int block, int top_k,
                                   hipStream_t stream) {
-  // LDS for scores: QT * NR * 256 bytes, kept <= 64 KiB.
-  constexpr int QTM = NR <= 16 ? 16 : 256 / NR;
+  // Queries per workgroup.  Scoring runs on as many lanes as there are candidates and
+  // selection on one wave per query, so a workgroup's time grows with its queries; small
+  // tiles keep many workgroups resident (LDS for scores: QT * NR * 256 bytes) and were
+  // measured fastest (4 up to 256 candidates, 8 beyond).
+  constexpr int QTM = NR <= 4 ? 4 : NR <= 32 ? 8 : 4;
   if (n_q == 1)
     return launch_index_t<T, NR, 1>(iq, cmp, kv_lens, sel, sel_scores, batch, n_q, h_idx, d_idx,
                                     max_blocks, block, top_k, stream);
