@@ -7,13 +7,22 @@
 // HBM-bound: every selected key/value byte is read once.  The token list of a sequence
 // (selected blocks in ascending order, then the trailing tokens) is cut into 64-key
 // chunks; a workgroup handles one (sequence, KV head, split) = a contiguous run of those
-// chunks and streams them through LDS, double-buffered, with fully coalesced 16-byte loads
-// of whole key/value rows.  The G query heads sharing the KV head form the 16 MFMA rows
-// (rows >= G are zero).  Each of the 4 waves takes 16 keys of a chunk:
-//   S^T = K . Q^T on 16x16x32 MFMAs, O^T += V^T . P^T on 16x16x16 MFMAs,
+// chunks.  Key and value rows go global -> LDS directly (global_load_lds_dwordx4, no
+// registers) through a ring of NS stages, so NS-1 chunks are always in flight while one
+// is used; the loads are issued outside the compiler's view and waited for by count.  The
+// G query heads sharing the KV head form the 16 MFMA rows (rows >= G are zero).  Each of
+// the 4 waves takes 16 keys of a chunk:
+//   S^T = K . Q^T on 16x16x32 MFMAs (A = K rows from LDS),
+//   O^T += V^T . P^T on 16x16x16 MFMAs (A = V^T through the LDS transpose read),
 // with per-wave online softmax; the waves' partial states meet in LDS at the end.  With
 // more than one split, each split writes a normalised partial output and its
 // log-sum-exp to the caller's workspace and a small merge kernel combines them.
+//
+// LDS layout of a stage: K rows, then V rows, each row D*2 bytes with its 16-byte units
+// permuted by XOR (K: with r & (D/8 - 1); V: with 2 * (r & (D/16 - 1))).  Every LDS-direct
+// load instruction then fetches whole rows (full cache lines), and the operand reads of a
+// wave (16 rows x one unit for K, 16 rows x 32 bytes for the V transpose read) spread over
+// all banks.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -22,31 +31,35 @@
 namespace qsa {
 
 namespace {
-constexpr int KC = 64;
-constexpr int kTargetWorkgroups = 1024;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+constexpr int KC = 64;  // keys per chunk
+constexpr int NS = 4;   // LDS stages
 
 __device__ __forceinline__ f32x4 mfma16x16x16_bf16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<s16x4>(a), bitcast<s16x4>(b), c, 0, 0, 0);
 }
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return 2 * (r & (D / 16 - 1)); }
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(
+__global__ __launch_bounds__(256, 1) void decode_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ kv_lens,
     const int32_t* __restrict__ sel, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int max_len, int h_q, int h_kv,
     int G, int block, int top_k, float scale_log2, int nsplit) {
-  constexpr int NC16 = D / 8;
-  constexpr int KIT = KC * NC16 / 256;
-  constexpr int VQ = KC / 4 * NC16;
-  constexpr int NQT = D / 32;  // k-steps of S^T (32 dims each)
-  constexpr int NDT = D / 16;  // 16-row d tiles of O^T
+  constexpr int NQT = D / 32;   // k-steps of S^T = K slabs
+  constexpr int NDT = D / 16;   // 16-row d tiles of O^T = V slabs
+  constexpr int TILE = KC * D;  // elements of one K (or V) chunk
+  constexpr int NU = D / 8;       // 16-byte units per row
+  constexpr int RPI = 64 / NU;    // rows per LDS-direct instruction (1 KB)
+  constexpr int KI = KC / 4 / RPI;  // instructions per wave per K (or V) chunk: 16 rows each
+  constexpr int DPC = 2 * KI;     // LDS-direct instructions per wave per chunk
+  static_assert(2 * DPC < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * KC];
+  __shared__ __attribute__((aligned(16))) uint16_t ring[NS * 2 * TILE];
   __shared__ int32_t list[kMaxTopK];
   __shared__ int32_t list_n;
   __shared__ float wm[4][16];
@@ -57,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_uniform(tid >> 6);
 
   int len = kv_lens[b];
   len = len < 0 ? 0 : (len > max_len ? max_len : len);
@@ -85,12 +98,13 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(
   const int nchunks = mv * nsub + tunits;
   const int c_begin = (int)((long long)nchunks * split / nsplit);
   const int c_end = (int)((long long)nchunks * (split + 1) / nsplit);
+  const int nch = c_end - c_begin;
 
-  const size_t kv_row = (size_t)h_kv * D;
+  const uint32_t kv_row = (uint32_t)h_kv * D;  // elements between consecutive tokens
   const uint16_t* kbase = kc + ((size_t)b * max_len * h_kv + g) * D;
   const uint16_t* vbase = vc + ((size_t)b * max_len * h_kv + g) * D;
 
-  auto chunk_keys = [&](int u, int& key0, int& ck) {
+  auto chunk_keys = [&](int u, int& key0, int& ck) __attribute__((always_inline)) {
     if (u < mv * nsub) {
       const int j = list[u / nsub], sub = u % nsub;
       key0 = j * block + sub * KC;
@@ -102,54 +116,29 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(
     }
   };
 
-  u32x4 kreg[KIT];
-  u32x4 vreg[4];
-  auto load_chunk = [&](int u) {
+  // LDS-direct loads of chunk u into stage u % NS: each instruction fills 1 KB = RPI whole
+  // rows; wave w fills rows 16w .. 16w+15 of K and of V; lane -> (row lane / NU, physical
+  // unit lane % NU) and fetches the logical unit the swizzle maps there.  Rows past the
+  // chunk re-read its last key (their scores are masked).
+  const uint32_t ring_lds = lds_addr(ring);
+  const int l_row = lane / NU, l_unit = lane % NU;
+  auto issue = [&](int u) __attribute__((always_inline)) {
     int key0, ck;
     chunk_keys(u, key0, ck);
+    const uint32_t st = ring_lds + (uint32_t)(u % NS) * (2 * TILE * 2);
 #pragma unroll
-    for (int i = 0; i < KIT; ++i) {
-      const int e = i * 256 + tid;
-      const int r = e / NC16, c = e % NC16;
-      kreg[i] = (r < ck) ? *reinterpret_cast<const u32x4*>(kbase + (size_t)(key0 + r) * kv_row + c * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < VQ) {
-      const int c = tid % NC16, quad = tid / NC16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = quad * 4 + i;
-        vreg[i] = (r < ck) ? *reinterpret_cast<const u32x4*>(vbase + (size_t)(key0 + r) * kv_row + c * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < KI; ++i) {
+      const int r0 = 16 * wave + RPI * i;
+      const int r = r0 + l_row;
+      const uint32_t grow = (uint32_t)(key0 + min(r, ck - 1));
+      global_to_lds16_untracked(kbase + grow * kv_row + 8 * (l_unit ^ k_swz<D>(r)), st + r0 * D * 2);
+      global_to_lds16_untracked(vbase + grow * kv_row + 8 * (l_unit ^ v_swz<D>(r)),
+                                st + TILE * 2 + r0 * D * 2);
     }
   };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KIT; ++i) {
-      const int e = i * 256 + tid;
-      const int r = e / NC16, c = e % NC16;
-      *reinterpret_cast<u32x4*>(&Ks[buf][r * D + ((c ^ (r & (NC16 - 1))) * 8)]) = kreg[i];
-    }
-    if (tid < VQ) {
-      const int c = tid % NC16, quad = tid / NC16;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int d = c * 8 + dd;
-        const int w = dd >> 1;
-        uint32_t lo, hi;
-        if (dd & 1) {
-          lo = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
-          hi = (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u);
-        } else {
-          lo = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
-          hi = (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16);
-        }
-        const int unit = quad ^ ((d >> 1) & 15);
-        *reinterpret_cast<u32x2*>(&Vt[buf][d * KC + unit * 4]) = u32x2{lo, hi};
-      }
-    }
-  };
+
+  int issued = 0;
+  for (; issued < NS - 1 && issued < nch; ++issued) issue(c_begin + issued);
 
   // query rows: lane holds row nr = lane & 15 (query head g*G + nr when nr < G)
   const int nr = lane & 15;
@@ -161,6 +150,9 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
       u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qp + t * 32) : u32x4{0u, 0u, 0u, 0u};
+      // opaque to the optimizer: Q stays in registers (a re-load inside the loop would also
+      // wait for the key/value loads in flight)
+      keep_in_register(w);
       qreg[t] = bitcast<bf16x8>(w);
     }
   }
@@ -171,25 +163,41 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (c_begin < c_end) {
-    load_chunk(c_begin);
-    store_chunk(0);
+  // per-lane byte offsets of the operand reads inside a stage (this wave's 16 keys):
+  //   K: row kw + nr, logical unit 4t + quarter;
+  //   V (transpose read): row kw + 4*quarter + nr / 4, columns 16*dt + 4*(nr % 4) .. +3.
+  const int kw = wave * 16;
+  int k_off[NQT], v_off[NDT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) k_off[t] = (kw + nr) * D * 2 + 16 * ((4 * t + quarter) ^ k_swz<D>(kw + nr));
+  {
+    const int vr = kw + 4 * quarter + (nr >> 2);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      v_off[dt] = TILE * 2 + vr * D * 2 + 16 * ((2 * dt + ((nr & 3) >> 1)) ^ v_swz<D>(vr)) + 8 * (nr & 1);
   }
-  __syncthreads();
-  int buf = 0;
-  for (int u = c_begin; u < c_end; ++u) {
-    const bool have_next = u + 1 < c_end;
-    if (have_next) load_chunk(u + 1);
+
+  for (int i = 0; i < nch; ++i) {
+    // chunk i must have landed; the (at most NS-2) chunks after it may stay in flight
+    const int after = issued - i - 1;
+    if (after >= 2) wait_vmcnt<2 * DPC>();
+    else if (after == 1) wait_vmcnt<DPC>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();
+    // every wave is past chunk i-1: its stage takes chunk i+NS-1
+    if (issued < nch) {
+      issue(c_begin + issued);
+      ++issued;
+    }
+    const int u = c_begin + i;
     int key0, ck;
     chunk_keys(u, key0, ck);
-    const int kw = wave * 16;  // this wave's keys inside the chunk
+    const char* st = reinterpret_cast<const char*>(ring + (u % NS) * (2 * TILE));
     if (kw < ck) {
       f32x4 s{0.f, 0.f, 0.f, 0.f};
-      const int kr = kw + nr;
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
-        const int c = 4 * t + quarter;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[buf][kr * D + ((c ^ (kr & (NC16 - 1))) * 8)]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + k_off[t]);
         s = mfma16x16x32(a, qreg[t], s);
       }
       float mx = -__builtin_inff();
@@ -211,20 +219,18 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(
       const float e3 = __builtin_amdgcn_exp2f(s[3] - m_use);
       l_run = l_run * alpha + ((e0 + e1) + (e2 + e3));
       m_run = m_new;
+      // B operand: P^T at keys 4*quarter + {0..3}, column nr (the S^T accumulator layout)
       const u32x2 pb{pack_bf16x2(e0, e1), pack_bf16x2(e2, e3)};
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         O[dt] *= alpha;
-        const int d = dt * 16 + nr;
-        const int unit = (4 * wave + quarter) ^ ((d >> 1) & 15);
-        const u32x2 a = *reinterpret_cast<const u32x2*>(&Vt[buf][d * KC + unit * 4]);
+        // A operand: V^T rows d = 16*dt + nr, keys 4*quarter + {0..3} of this wave
+        const u32x2 a = lds_read_tr16(reinterpret_cast<const uint16_t*>(st + v_off[dt]));
         O[dt] = mfma16x16x16_bf16(a, pb, O[dt]);
       }
     }
-    if (have_next) store_chunk(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
   }
+  __syncthreads();  // every wave is done with the ring before it holds the partial outputs
 
   // ---- combine the 4 waves (rows nr, d = dt*16 + 4*quarter + r) ----
   float lsum = l_run + __shfl_xor(l_run, 16);
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(
     wm[wave][nr] = m_run;
     wl[wave][nr] = lsum;
   }
-  float* wo = reinterpret_cast<float*>(&Ks[0][0]);  // [4][D][16] floats, fits in Ks
+  float* wo = reinterpret_cast<float*>(ring);  // [4][D][16] floats, fits in the ring
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -293,15 +299,36 @@ bool decode_bf16_supported(int group, int d, int block, int top_k) {
   return block >= 1 && block <= 1024 && top_k >= 1 && top_k <= kMaxTopK;
 }
 
+// Workgroups that run at once: one per CU (the LDS ring takes 128 KB at D = 128).
+static int decode_slots() {
+  static int slots = 0;
+  if (slots == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    slots = cus;
+  }
+  return slots;
+}
+
+// Splits of each (sequence, KV head): the smallest count whose workgroups fill at least 90%
+// of whole rounds of the workgroups that run at once, with at least ~4 chunks per split.
 int decode_num_splits(int batch, int h_kv, int block, int top_k) {
   const long long units = (long long)batch * h_kv;
   if (units <= 0) return 1;
-  long long want = (kTargetWorkgroups + units - 1) / units;
+  const long long slots = decode_slots();
   const long long chunks = (long long)top_k * ((block + KC - 1) / KC) + (block + KC - 2) / KC;
-  if (want > chunks) want = chunks;
-  if (want > 32) want = 32;
-  if (want < 1) want = 1;
-  return (int)want;
+  long long max_split = chunks / 4;
+  if (max_split > 32) max_split = 32;
+  if (max_split < 1) max_split = 1;
+  for (long long s = 1; s <= max_split; ++s) {
+    const long long wgs = units * s;
+    const long long rounds = (wgs + slots - 1) / slots;
+    if (wgs * 10 >= rounds * slots * 9) return (int)s;
+  }
+  return (int)max_split;
 }
 
 size_t decode_workspace_bytes(int batch, int h_q, int d, int nsplit) {

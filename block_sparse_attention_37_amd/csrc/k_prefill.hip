@@ -42,8 +42,6 @@ constexpr int KC = 64;   // keys per LDS chunk
 constexpr int NW = 8;    // waves per workgroup
 constexpr int NS = 4;    // LDS stages (chunks in flight + the one being used)
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
 template <int N>
 struct Int {
   static constexpr int value = N;
@@ -78,25 +76,6 @@ __device__ __forceinline__ bool advance(const uint32_t* bm, int words, int nsub,
   return next_block(bm, words, it);
 }
 
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-#endif
-}
-
-// Workgroup barrier without the memory fence __syncthreads() implies: that fence would
-// drain every outstanding LDS-direct load.  The loop waits for exactly the chunk it needs
-// (wait_vmcnt) before the barrier; the LDS it reads was filled only by those loads, and
-// the clobber keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_no_fence() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_barrier" ::: "memory");
-#endif
-}
-
 // Instruction-order hints for the scheduler (no effect on results): mask selects the
 // instruction class (0x8 MFMA, 0x100 LDS read), n how many of them come next.
 template <int MASK, int N>
@@ -127,15 +106,6 @@ __device__ __forceinline__ float pair_sum(float x) {
 #endif
 }
 
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  return bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
-#else
-  (void)p;
-  return u32x2{0u, 0u};
-#endif
-}
 
 // LDS layout of one stage (byte offsets), chosen so that every operand read of a lane is
 // one base register plus an immediate and every read is free of bank conflicts:

@@ -130,4 +130,37 @@ __device__ __forceinline__ To bitcast(const From& f) {
   return __builtin_bit_cast(To, f);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+#endif
+}
+
+// Workgroup barrier without the memory fence __syncthreads() implies: that fence would
+// drain every outstanding LDS-direct load.  Callers wait for exactly the loads they need
+// (wait_vmcnt) before the barrier; the clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_barrier" ::: "memory");
+#endif
+}
+
+// LDS transpose read (ds_read_b64_tr_b16): inside each group of 16 lanes, lane i receives
+// element i % 4 of the four 16-bit elements that lanes 4j + i / 4 (j = 0..3) point at.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+#else
+  (void)p;
+  return u32x2{0u, 0u};
+#endif
+}
+
 }  // namespace qsa
