@@ -86,6 +86,15 @@ __device__ __forceinline__ void sched_group() {
 }
 constexpr int kSchedMfma = 0x8;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kReadAhead = 4;  // LDS operand reads issued ahead of their MFMA (measured best)
+
+// Issue priority of this wave among the waves of its SIMD (s_setprio).
+template <int P>
+__device__ __forceinline__ void set_wave_priority() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_setprio(P);
+#endif
+}
 
 // max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap leaves each lane with
 // its own value and its partner's, in some order, which max and sum do not care about.
@@ -287,6 +296,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   bf16x8 P[4];
 
   auto mfma_phase = [&](int c, bool do_s, bool do_pv) __attribute__((always_inline)) {
+    // the wave in its matrix phase goes first when both waves of a SIMD can issue
+    set_wave_priority<2>();
     const char* Ks = reinterpret_cast<const char*>(ring + (c % NS) * (2 * TILE));
     const char* Vp = reinterpret_cast<const char*>(ring + ((c + NS - 1) % NS) * (2 * TILE));
     if (do_s) {
@@ -300,14 +311,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
           S[kt] = mfma32x32x16(a, qreg[t], S[kt]);
         }
       }
-      // operand reads run two MFMAs ahead
-      sched_group<kSchedDsRead, 2>();
+      // operand reads run kReadAhead MFMAs ahead
+      sched_group<kSchedDsRead, kReadAhead>();
 #pragma unroll
-      for (int i = 0; i < 2 * NKS - 2; ++i) {
+      for (int i = 0; i < 2 * NKS - kReadAhead; ++i) {
         sched_group<kSchedMfma, 1>();
         sched_group<kSchedDsRead, 1>();
       }
-      sched_group<kSchedMfma, 2>();
+      sched_group<kSchedMfma, kReadAhead>();
     }
     if (do_pv) {
       // A operand of 16-key step st: V at d = 32*dt + (lane % 32), keys 16st + 4*half +
@@ -324,15 +335,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
           O[dt] = mfma32x32x16(a, P[st], O[dt]);
         }
       }
-      // two transpose reads per MFMA, running two MFMAs ahead
-      sched_group<kSchedDsRead, 4>();
+      // two transpose reads per MFMA, running kReadAhead MFMAs ahead
+      sched_group<kSchedDsRead, 2 * kReadAhead>();
 #pragma unroll
-      for (int i = 0; i < 4 * NDT - 2; ++i) {
+      for (int i = 0; i < 4 * NDT - kReadAhead; ++i) {
         sched_group<kSchedMfma, 1>();
         sched_group<kSchedDsRead, 2>();
       }
-      sched_group<kSchedMfma, 2>();
+      sched_group<kSchedMfma, kReadAhead>();
     }
+    set_wave_priority<0>();
   };
 
   // S holds the scores of a whole 64-key chunk; keys past the chunk (clamped rows, finite)
