@@ -9,9 +9,11 @@
 A step is one pass of the whole QSA path over one batch of synthetic input:
   prefill workloads: key-block compression -> indexer scores + top-k selection
                      -> block-sparse attention;
-  decode workloads:  indexer scores + top-k over the cached compressed keys ->
-                     block-sparse decode attention (the compressed indexer state
-                     of the cached prefix is computed once, before timing).
+  decode workloads:  indexer step (completes the compressed block the newest
+                     token finishes, then scores + top-k over the cached compressed
+                     keys) -> block-sparse decode attention (the compressed indexer
+                     state of the prefix before the newest token is computed once,
+                     before timing).
 Inputs are resident in HBM before the timed region starts.  ``value`` is
 tokens/s of the whole step (prefill: batch*seq tokens, decode: batch tokens).
 
@@ -159,9 +161,10 @@ def setup_decode(w, dev):
         q[b] = S.to_torch(s["q"]).to(dev)
         iq[b, 0] = S.to_torch(s["iq"]).to(dev)
     kvl = torch.from_numpy(lens).to(dev)
-    cmp = Q.compress_keys(ik, w.block, kv_lens=kvl)   # indexer state, not timed
-    del ik
-    plan = Q.DecodePlan(q, kc, vc, kvl, iq, cmp, w.block, w.top_k, w.sm_scale)
+    # indexer state of the prefix before the newest token (not timed); each step's index call
+    # completes the block the newest token finishes (qsa_index_topk_decode)
+    cmp = Q.compress_keys(ik, w.block, kv_lens=kvl - 1)
+    plan = Q.DecodePlan(q, kc, vc, kvl, iq, cmp, w.block, w.top_k, w.sm_scale, ik_cache=ik)
     return plan, lens
 
 

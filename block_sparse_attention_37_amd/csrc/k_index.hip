@@ -18,19 +18,28 @@
 //      the scores finds the m-th largest value with wave ballots; ties at that value go
 //      to the lowest block ids; the kept ids come out in ascending order via ballot
 //      prefix counts.  No sorting network, no atomics: the result is deterministic.
+#include "block_mean.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 
-template <typename T, int NR, int QT>
+// UPD_DI > 0 (decode, QT == 1, d_idx == UPD_DI): before scoring, a sequence whose length L
+// is a positive multiple of `block` gets the block its newest token completes,
+// j = L / block - 1, compressed from the indexer-key cache `ik` (BlockMean, bit-identical to
+// the compression kernel) and written to cmp; that block is scored from the LDS copy.
+template <typename T, int NR, int QT, int UPD_DI>
 __global__ __launch_bounds__(256) void index_topk_kernel(
-    const T* __restrict__ iq, const float* __restrict__ cmp, const int32_t* __restrict__ kv_lens,
+    const T* __restrict__ iq, const float* cmp_in, const int32_t* __restrict__ kv_lens,
     int32_t* __restrict__ sel, float* __restrict__ sel_scores, int n_q, int h_idx, int d_idx,
-    int max_blocks, int block, int top_k) {
+    int max_blocks, int block, int top_k, const T* __restrict__ ik, int ik_max_len,
+    float* cmp_out) {
   constexpr int NC = NR * 64;
   __shared__ float qs[128][QT];  // d_idx <= 128
   __shared__ float sc[QT][NC];
+  __shared__ float part[UPD_DI > 0 ? BlockMean<T, (UPD_DI > 0 ? UPD_DI : 32)>::SCRATCH : 1];
+  __shared__ float newrow[UPD_DI > 0 ? UPD_DI : 1];
+  const float* cmp = cmp_in;
 
   const int b = blockIdx.y;
   const int i0 = blockIdx.x * QT;
@@ -38,6 +47,20 @@ __global__ __launch_bounds__(256) void index_topk_kernel(
   const int len = kv_lens ? kv_lens[b] : n_q;
   const int nq_here = min(QT, n_q - i0);
   const int cap = min(max_blocks, NC);
+
+  int j_new = -1;  // block compressed here (decode state update), scored from newrow
+  if constexpr (UPD_DI > 0) {
+    static_assert(QT == 1, "the state update is a decode step");
+    if (len > 0 && len <= ik_max_len && len % block == 0 && len / block <= max_blocks) {
+      j_new = len / block - 1;
+      const float m = BlockMean<T, UPD_DI>::run(
+          ik + ((size_t)b * ik_max_len + (size_t)j_new * block) * UPD_DI, block, part, tid);
+      if (tid < UPD_DI) {
+        newrow[tid] = m;
+        cmp_out[((size_t)b * max_blocks + j_new) * UPD_DI + tid] = m;
+      }
+    }
+  }
 
   // 1. head-summed indexer queries
   for (int e = tid; e < QT * d_idx; e += 256) {
@@ -55,7 +78,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(
   const int p_last = len - n_q + i0 + nq_here - 1;
   const int n_last = max(0, min((p_last + 1) / block, cap));
   for (int j = tid; j < n_last; j += 256) {
-    const float* row = cmp + ((size_t)b * max_blocks + j) * d_idx;
+    const float* row = (UPD_DI > 0 && j == j_new) ? newrow : cmp + ((size_t)b * max_blocks + j) * d_idx;
     float acc[QT];
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi) acc[qi] = 0.f;
@@ -125,15 +148,16 @@ __global__ __launch_bounds__(256) void index_topk_kernel(
   }
 }
 
-template <typename T, int NR, int QT>
+template <typename T, int NR, int QT, int UPD_DI>
 static hipError_t launch_index_t(const void* iq, const float* cmp, const int32_t* kv_lens,
                                  int32_t* sel, float* sel_scores, int batch, int n_q, int h_idx,
                                  int d_idx, int max_blocks, int block, int top_k,
+                                 const void* ik, int ik_max_len, float* cmp_out,
                                  hipStream_t stream) {
   dim3 grid((n_q + QT - 1) / QT, batch);
-  hipLaunchKernelGGL((index_topk_kernel<T, NR, QT>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((index_topk_kernel<T, NR, QT, UPD_DI>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(iq), cmp, kv_lens, sel, sel_scores, n_q, h_idx, d_idx,
-                     max_blocks, block, top_k);
+                     max_blocks, block, top_k, static_cast<const T*>(ik), ik_max_len, cmp_out);
   return hipGetLastError();
 }
 
@@ -141,27 +165,36 @@ template <typename T, int NR>
 static hipError_t launch_index_nr(const void* iq, const float* cmp, const int32_t* kv_lens,
                                   int32_t* sel, float* sel_scores, int batch, int n_q, int h_idx,
                                   int d_idx, int max_blocks, int block, int top_k,
+                                  const void* ik, int ik_max_len, float* cmp_out,
                                   hipStream_t stream) {
   // Queries per workgroup.  Scoring runs on as many lanes as there are candidates and
   // selection on one wave per query, so a workgroup's time grows with its queries; small
   // tiles keep many workgroups resident (LDS for scores: QT * NR * 256 bytes) and were
   // measured fastest (4 up to 256 candidates, 8 beyond).
   constexpr int QTM = NR <= 4 ? 4 : NR <= 32 ? 8 : 4;
-  if (n_q == 1)
-    return launch_index_t<T, NR, 1>(iq, cmp, kv_lens, sel, sel_scores, batch, n_q, h_idx, d_idx,
-                                    max_blocks, block, top_k, stream);
-  return launch_index_t<T, NR, QTM>(iq, cmp, kv_lens, sel, sel_scores, batch, n_q, h_idx, d_idx,
-                                    max_blocks, block, top_k, stream);
+#define QSA_IDX(qt, upd)                                                                   \
+  return launch_index_t<T, NR, qt, upd>(iq, cmp, kv_lens, sel, sel_scores, batch, n_q, h_idx, \
+                                        d_idx, max_blocks, block, top_k, ik, ik_max_len,      \
+                                        cmp_out, stream)
+  if (cmp_out != nullptr) {  // decode step with the indexer-state update
+    if (d_idx == 32) QSA_IDX(1, 32);
+    if (d_idx == 64) QSA_IDX(1, 64);
+    QSA_IDX(1, 128);
+  }
+  if (n_q == 1) QSA_IDX(1, 0);
+  QSA_IDX(QTM, 0);
+#undef QSA_IDX
 }
 
 template <typename T>
 static hipError_t launch_index_dt(const void* iq, const float* cmp, const int32_t* kv_lens,
                                   int32_t* sel, float* sel_scores, int batch, int n_q, int h_idx,
                                   int d_idx, int max_blocks, int block, int top_k,
+                                  const void* ik, int ik_max_len, float* cmp_out,
                                   hipStream_t stream) {
 #define QSA_NR(nr)                                                                           \
   return launch_index_nr<T, nr>(iq, cmp, kv_lens, sel, sel_scores, batch, n_q, h_idx, d_idx, \
-                                max_blocks, block, top_k, stream)
+                                max_blocks, block, top_k, ik, ik_max_len, cmp_out, stream)
   const int need = max_blocks;
   if (need <= 128) QSA_NR(2);
   if (need <= 256) QSA_NR(4);
@@ -179,9 +212,21 @@ hipError_t launch_index_topk(const void* iq, const float* cmp, const int32_t* kv
   if (batch == 0 || n_q == 0) return hipSuccess;
   if (bf16)
     return launch_index_dt<uint16_t>(iq, cmp, kv_lens, sel, sel_scores, batch, n_q, h_idx, d_idx,
-                                     max_blocks, block, top_k, stream);
+                                     max_blocks, block, top_k, nullptr, 0, nullptr, stream);
   return launch_index_dt<float>(iq, cmp, kv_lens, sel, sel_scores, batch, n_q, h_idx, d_idx,
-                                max_blocks, block, top_k, stream);
+                                max_blocks, block, top_k, nullptr, 0, nullptr, stream);
+}
+
+hipError_t launch_index_topk_decode(const void* iq, const void* ik, float* cmp,
+                                    const int32_t* kv_lens, int32_t* sel, float* sel_scores,
+                                    int batch, int max_len, int h_idx, int d_idx, int max_blocks,
+                                    int block, int top_k, bool bf16, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  if (bf16)
+    return launch_index_dt<uint16_t>(iq, cmp, kv_lens, sel, sel_scores, batch, 1, h_idx, d_idx,
+                                     max_blocks, block, top_k, ik, max_len, cmp, stream);
+  return launch_index_dt<float>(iq, cmp, kv_lens, sel, sel_scores, batch, 1, h_idx, d_idx,
+                                max_blocks, block, top_k, ik, max_len, cmp, stream);
 }
 
 }  // namespace qsa

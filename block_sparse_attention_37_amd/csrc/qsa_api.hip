@@ -110,6 +110,37 @@ qsa_status qsa_index_topk(const void* iq, const float* cmp, const int32_t* kv_le
                   "qsa_index_topk");
 }
 
+qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cmp,
+                                 const int32_t* kv_lens, int32_t* sel, float* sel_scores,
+                                 int batch, int max_len, int h_idx, int d_idx, int max_blocks,
+                                 int block, int top_k, qsa_dtype dt, hipStream_t stream) {
+  QSA_REQUIRE(dtype_ok(dt), QSA_ERR_INVALID_ARGUMENT, "dt must be QSA_F32 or QSA_BF16");
+  QSA_REQUIRE(batch >= 0 && max_len >= 1 && max_blocks >= 0, QSA_ERR_INVALID_ARGUMENT,
+              "batch and max_blocks must be >= 0, max_len >= 1");
+  QSA_REQUIRE(h_idx >= 1 && d_idx >= 1 && block >= 1, QSA_ERR_INVALID_ARGUMENT,
+              "h_idx, d_idx and block must be >= 1");
+  QSA_REQUIRE(top_k >= 1, QSA_ERR_INVALID_ARGUMENT, "top_k must be >= 1 (got %d)", top_k);
+  QSA_REQUIRE(d_idx == 32 || d_idx == 64 || d_idx == 128, QSA_ERR_UNSUPPORTED,
+              "d_idx %d not supported (32, 64, 128)", d_idx);
+  QSA_REQUIRE(h_idx <= 64, QSA_ERR_UNSUPPORTED, "h_idx %d not supported (<= 64)", h_idx);
+  QSA_REQUIRE(top_k <= qsa::kMaxTopK, QSA_ERR_UNSUPPORTED, "top_k %d not supported (<= %d)",
+              top_k, qsa::kMaxTopK);
+  QSA_REQUIRE(max_blocks <= qsa::kIndexMaxBlocks, QSA_ERR_UNSUPPORTED,
+              "max_blocks %d not supported (<= %d)", max_blocks, qsa::kIndexMaxBlocks);
+  QSA_REQUIRE(block <= 1024, QSA_ERR_UNSUPPORTED, "block %d not supported (<= 1024)", block);
+  if (batch == 0) return ok();
+  QSA_PTR(iq, "iq");
+  QSA_PTR(ik_cache, "ik_cache");
+  QSA_PTR(kv_lens, "kv_lens");
+  QSA_PTR(sel, "sel");
+  QSA_OPT_PTR(sel_scores, "sel_scores");
+  if (max_blocks > 0) QSA_PTR(cmp, "cmp");
+  return from_hip(qsa::launch_index_topk_decode(iq, ik_cache, cmp, kv_lens, sel, sel_scores,
+                                                batch, max_len, h_idx, d_idx, max_blocks, block,
+                                                top_k, dt == QSA_BF16, stream),
+                  "qsa_index_topk_decode");
+}
+
 qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                    const int32_t* sel, void* out, float* lse, int batch, int seq,
                                    int h_q, int h_kv, int d, int block, int top_k,

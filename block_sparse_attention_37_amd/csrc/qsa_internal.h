@@ -20,6 +20,14 @@ hipError_t launch_index_topk(const void* iq, const float* cmp, const int32_t* kv
                              int d_idx, int max_blocks, int block, int top_k, bool bf16,
                              hipStream_t stream);
 
+// Decode step of the indexer with the state update: compresses the block each sequence's
+// newest token completes (from the indexer-key cache), writes it to cmp, then scores and
+// selects for the one query per sequence.
+hipError_t launch_index_topk_decode(const void* iq, const void* ik, float* cmp,
+                                    const int32_t* kv_lens, int32_t* sel, float* sel_scores,
+                                    int batch, int max_len, int h_idx, int d_idx, int max_blocks,
+                                    int block, int top_k, bool bf16, hipStream_t stream);
+
 // bf16 prefill on matrix cores.  Returns hipErrorInvalidValue for shapes it is not built for.
 // A workgroup keeps the selection rows of its query positions (positions x top_k entries)
 // and a bitmap of the blocks it visits in LDS.

@@ -34,6 +34,7 @@ SIGNATURES = {
     "qsa_version": (_I, []),
     "qsa_compress_keys": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "qsa_index_topk": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "qsa_index_topk_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "qsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "qsa_sparse_attn_decode_workspace_size": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)]),
     "qsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -149,6 +150,37 @@ def index_topk(iq: torch.Tensor, cmp: torch.Tensor, block: int, top_k: int,
     dev = _dev(iq, cmp, kv_lens, out, out_scores)
     _call("qsa_index_topk", _ptr(iq), _ptr(cmp), _ptr(kv_lens), _ptr(out), _ptr(out_scores),
           batch, n_q, h_idx, d_idx, max_blocks, block, top_k, _dt(iq), _stream(dev))
+    return (out, out_scores) if out_scores is not None else out
+
+
+def index_topk_decode(iq: torch.Tensor, ik_cache: torch.Tensor, cmp: torch.Tensor,
+                      kv_lens: torch.Tensor, block: int, top_k: int, with_scores: bool = False,
+                      out: torch.Tensor | None = None, out_scores: torch.Tensor | None = None):
+    """One decode step of the indexer: compresses the block each sequence's newest token
+    completes into ``cmp`` (in place), then selects.  iq [batch, h_idx, d_idx] (or
+    [batch, 1, h_idx, d_idx]), ik_cache [batch, max_len, d_idx], cmp float32
+    [batch, max_blocks, d_idx], kv_lens int32 [batch] -> sel int32 [batch, 1, top_k]."""
+    if iq.dim() == 3:
+        iq = iq.unsqueeze(1)
+    batch, n_q, h_idx, d_idx = iq.shape
+    if n_q != 1:
+        raise ValueError("index_topk_decode takes one query per sequence")
+    max_len = ik_cache.shape[1]
+    max_blocks = cmp.shape[1]
+    _expect(ik_cache, (batch, max_len, d_idx), iq.dtype, "ik_cache")
+    _expect(cmp, (batch, max_blocks, d_idx), torch.float32, "cmp")
+    _expect(kv_lens, (batch,), torch.int32, "kv_lens")
+    if out is None:
+        out = torch.empty(batch, 1, top_k, dtype=torch.int32, device=iq.device)
+    _expect(out, (batch, 1, top_k), torch.int32, "sel")
+    if with_scores and out_scores is None:
+        out_scores = torch.empty(batch, 1, top_k, dtype=torch.float32, device=iq.device)
+    if out_scores is not None:
+        _expect(out_scores, (batch, 1, top_k), torch.float32, "sel_scores")
+    dev = _dev(iq, ik_cache, cmp, kv_lens, out, out_scores)
+    _call("qsa_index_topk_decode", _ptr(iq), _ptr(ik_cache), _ptr(cmp), _ptr(kv_lens), _ptr(out),
+          _ptr(out_scores), batch, max_len, h_idx, d_idx, max_blocks, block, top_k, _dt(iq),
+          _stream(dev))
     return (out, out_scores) if out_scores is not None else out
 
 
@@ -289,10 +321,12 @@ class PrefillPlan:
 
 class DecodePlan:
     """index/top-k -> sparse decode attention for fixed decode tensors; ``cmp``
-    is the caller's compressed indexer state of the cached prefix."""
+    is the caller's compressed indexer state of the cached prefix.  With
+    ``ik_cache`` the index step is qsa_index_topk_decode, which also completes the
+    compressed block that each sequence's newest token finishes."""
 
     def __init__(self, q, k_cache, v_cache, kv_lens, iq, cmp, block: int, top_k: int,
-                 sm_scale: float | None = None):
+                 sm_scale: float | None = None, ik_cache=None):
         batch, h_q, d = q.shape
         max_len, h_kv = k_cache.shape[1], k_cache.shape[2]
         h_idx, d_idx = iq.shape[-2:]
@@ -302,16 +336,24 @@ class DecodePlan:
         self.lse = torch.empty(batch, h_q, dtype=torch.float32, device=dev)
         self.workspace = decode_workspace(batch, h_q, h_kv, d, block, top_k, dev)
         scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
-        self._keep = (q, k_cache, v_cache, kv_lens, iq, cmp)
+        self._keep = (q, k_cache, v_cache, kv_lens, iq, cmp, ik_cache)
         self.dev = dev
-        self._index = (_ptr(iq), _ptr(cmp), _ptr(kv_lens), _ptr(self.sel), None, batch, 1, h_idx,
-                       d_idx, cmp.shape[1], block, top_k, _dt(iq))
+        if ik_cache is None:
+            self._index_fn = "qsa_index_topk"
+            self._index = (_ptr(iq), _ptr(cmp), _ptr(kv_lens), _ptr(self.sel), None, batch, 1,
+                           h_idx, d_idx, cmp.shape[1], block, top_k, _dt(iq))
+        else:
+            _expect(ik_cache, (batch, ik_cache.shape[1], d_idx), iq.dtype, "ik_cache")
+            self._index_fn = "qsa_index_topk_decode"
+            self._index = (_ptr(iq), _ptr(ik_cache), _ptr(cmp), _ptr(kv_lens), _ptr(self.sel), None,
+                           batch, ik_cache.shape[1], h_idx, d_idx, cmp.shape[1], block, top_k,
+                           _dt(iq))
         self._attn = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens), _ptr(self.sel),
                       _ptr(self.out), _ptr(self.lse), batch, max_len, h_q, h_kv, d, block, top_k,
                       scale, _ptr(self.workspace), self.workspace.numel(), _dt(q))
 
     def run_index(self):
-        _call("qsa_index_topk", *self._index, _stream(self.dev))
+        _call(self._index_fn, *self._index, _stream(self.dev))
 
     def run_attention(self):
         _call("qsa_sparse_attn_decode", *self._attn, _stream(self.dev))

@@ -117,6 +117,35 @@ qsa_status qsa_index_topk(const void* iq, const float* cmp, const int32_t* kv_le
                           int block, int top_k, qsa_dtype dt, hipStream_t stream);
 
 /*
+ * Steps 1-3 for one decode step, with the indexer state kept on the device (Qwen4-Exp
+ * usage tips: cached generation keeps the QSA indexer states on the device; config:
+ * indexer_compress_ratio consecutive keys are averaged into one index block).
+ *
+ * Sequence b has len_b = kv_lens[b] tokens; its newest token sits at p = len_b - 1 and its
+ * indexer key is already stored in ik_cache[b, p].  If len_b is a positive multiple of
+ * block, that token completes block j = len_b / block - 1: the call first writes
+ *
+ *   cmp[b, j, c] = (1/block) * sum_{s = j*block}^{j*block+block-1} ik_cache[b, s, c]
+ *
+ * bit-identical to what qsa_compress_keys computes for that block, then scores and selects
+ * exactly like qsa_index_topk with n_q = 1.  Rows of cmp for other blocks are only read:
+ * they must hold the compressed blocks of the prefix (from qsa_compress_keys or earlier
+ * calls of this function).
+ *
+ *   iq          [batch, h_idx, d_idx]        element type dt
+ *   ik_cache    [batch, max_len, d_idx]      element type dt
+ *   cmp         [batch, max_blocks, d_idx]   float32, read and updated in place
+ *   kv_lens     [batch] int32 (required); values in [1, min(max_len, max_blocks*block + block - 1)]
+ *   sel, sel_scores  as for qsa_index_topk with n_q = 1
+ * Invalid: kv_lens or ik_cache NULL.
+ * Supported: as qsa_index_topk.
+ */
+qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cmp,
+                                 const int32_t* kv_lens, int32_t* sel, float* sel_scores,
+                                 int batch, int max_len, int h_idx, int d_idx, int max_blocks,
+                                 int block, int top_k, qsa_dtype dt, hipStream_t stream);
+
+/*
  * Steps 4 + 5, prefill -- attention of every prompt token over its selected tokens
  * (Qwen4-Exp overview: the selected contiguous blocks plus the uncompressed trailing
  * block; usage tips: sparse token selection feeding softmax attention; config fields

@@ -73,6 +73,28 @@ def test_index_validation(qsa_lib):
     assert L.qsa_index_topk(*args(n_q=0)) == 0
 
 
+def test_index_decode_validation(qsa_lib):
+    L = qsa_lib
+    def call(**kw):
+        a = dict(iq=FAKE, ik=FAKE, cmp=FAKE, kvl=FAKE, sel=FAKE, sc=None, batch=4, max_len=1024,
+                 h_idx=4, d_idx=64, max_blocks=16, block=64, top_k=4, dt=1)
+        a.update(kw)
+        return L.qsa_index_topk_decode(a["iq"], a["ik"], a["cmp"], a["kvl"], a["sel"], a["sc"],
+                                       a["batch"], a["max_len"], a["h_idx"], a["d_idx"],
+                                       a["max_blocks"], a["block"], a["top_k"], a["dt"], None)
+    assert call(kvl=None) == INVALID
+    assert "kv_lens" in _err()
+    assert call(ik=None) == INVALID
+    assert "ik_cache" in _err()
+    assert call(top_k=0) == INVALID
+    assert call(max_len=0) == INVALID
+    assert call(d_idx=96) == UNSUPPORTED
+    assert call(top_k=300) == UNSUPPORTED
+    assert call(max_blocks=5000) == UNSUPPORTED
+    assert call(cmp=FAKE + 4) == INVALID
+    assert call(batch=0) == 0
+
+
 def test_prefill_validation(qsa_lib):
     L = qsa_lib
     def call(**kw):
@@ -97,12 +119,12 @@ def test_prefill_validation(qsa_lib):
 def test_decode_validation(qsa_lib):
     L = qsa_lib
     n = ctypes.c_size_t(0)
-    assert L.qsa_sparse_attn_decode_workspace_size(64, 32, 4, 128, 64, 32, ctypes.byref(n)) == 0
+    assert L.qsa_sparse_attn_decode_workspace_size(8, 32, 4, 128, 64, 32, ctypes.byref(n)) == 0
     need = n.value
-    assert need > 0  # 256 (sequence, KV head) pairs -> split work -> workspace
-    assert L.qsa_sparse_attn_decode_workspace_size(64, 32, 4, 128, 64, 32, None) == INVALID
+    assert need > 0  # 32 (sequence, KV head) pairs on 256 CUs -> split work -> workspace
+    assert L.qsa_sparse_attn_decode_workspace_size(8, 32, 4, 128, 64, 32, None) == INVALID
     def call(**kw):
-        a = dict(q=FAKE, kc=FAKE, vc=FAKE, kvl=FAKE, sel=FAKE, out=FAKE, lse=None, batch=64,
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, kvl=FAKE, sel=FAKE, out=FAKE, lse=None, batch=8,
                  max_len=32768, h_q=32, h_kv=4, d=128, block=64, top_k=32, scale=0.1, ws=FAKE,
                  wsb=need, dt=1)
         a.update(kw)

@@ -304,6 +304,63 @@ def test_decode_matches_prefill_rows(gpu):
         assert max_abs(out.float().cpu().numpy()[0], res["out"][0][p]) <= 2e-2
 
 
+@pytest.mark.parametrize("dt,d_idx", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_decode_index_state_update(gpu, dt, d_idx):
+    """qsa_index_topk_decode: the block each sequence's newest token completes is written to
+    cmp bit-identical to a compression of the whole prefix, rows of other blocks stay as they
+    were, and the selection equals qsa_index_topk's and passes the oracle check."""
+    w = _dw(f"state_{dt}_{d_idx}", batch=6, max_len=208, block=16, top_k=3, h_q=8, h_kv=2,
+            d=64, dtype=dt, d_idx=d_idx, h_idx=3)
+    lens = np.array([16, 17, 32, 48, 100, 208], dtype=np.int32)  # 16, 32, 48, 208 complete a block
+    say(f"case {w.name}")
+    q, kc, vc, ik, iq, keep = gpu_decode_setup(w, lens, gpu, seqs=set(range(w.batch)))
+    kvl = torch.from_numpy(lens).to(gpu)
+    nb = w.max_len // w.block
+    cmp = torch.full((w.batch, nb, w.d_idx), float("nan"), dtype=torch.float32, device=gpu)
+    Q.compress_keys(ik, w.block, kv_lens=kvl - 1, out=cmp)  # state before the newest token
+    sel = Q.index_topk_decode(iq, ik, cmp, kvl, w.block, w.top_k)
+    full = Q.compress_keys(ik, w.block, kv_lens=kvl)
+    ref = Q.index_topk(iq.reshape(w.batch, 1, w.h_idx, w.d_idx), full, w.block, w.top_k,
+                       kv_lens=kvl)
+    torch.cuda.synchronize()
+    c, f = cmp.cpu().numpy(), full.cpu().numpy()
+    for b, L in enumerate(lens):
+        n = int(L) // w.block
+        assert np.array_equal(c[b, :n].view(np.uint32), f[b, :n].view(np.uint32)), f"seq {b}"
+        assert np.all(np.isnan(c[b, n:])), f"seq {b}: rows past the complete blocks written"
+    assert torch.equal(sel, ref)
+    for b, sq in keep.items():
+        cmp_o = O.compress_keys(S.to_f64(sq["ik"]), w.block)
+        fails, _ = check_selection(sel.cpu().numpy()[b], S.to_f64(sq["iq"])[None], cmp_o,
+                                   int(lens[b]), w.block, w.top_k)
+        assert not fails, f"seq {b}: {fails}"
+
+
+def test_decode_index_state_streaming(gpu):
+    """Tokens appended one at a time (prefix of 37, then 83 decode steps over block ends):
+    after every step the state equals the oracle's compression of the prefix and the
+    selection passes the oracle check."""
+    w = _wl("stream", seq=120, block=16, top_k=3, h_q=8, h_kv=2, d=64, h_idx=3, d_idx=64,
+            query_mean=True, plant_frac=0.2)
+    inp = S.prefill_inputs(w)
+    ik = _t(inp["ik"], gpu)[None]  # cache rows >= the current length are never read
+    iq_all = _t(inp["iq"], gpu)
+    ik64, iq64 = S.to_f64(inp["ik"]), S.to_f64(inp["iq"])
+    L0 = 37
+    kvl = torch.tensor([L0], dtype=torch.int32, device=gpu)
+    cmp = Q.compress_keys(ik, w.block, kv_lens=kvl)
+    for L in range(L0 + 1, w.seq + 1):
+        kvl.fill_(L)
+        sel = Q.index_topk_decode(iq_all[L - 1][None], ik, cmp, kvl, w.block, w.top_k)
+        torch.cuda.synchronize()
+        cmp_o = O.compress_keys(ik64[:L], w.block)
+        n = L // w.block
+        assert max_abs(cmp.cpu().numpy()[0, :n], cmp_o) <= 1e-5, f"L={L}: state"
+        fails, _ = check_selection(sel.cpu().numpy()[0], iq64[L - 1][None], cmp_o, L, w.block,
+                                   w.top_k)
+        assert not fails, f"L={L}: {fails}"
+
+
 def test_decode_bf16_b64_full(gpu):
     w = S.WORKLOADS["decode_bf16_b64"]
     lens = S.decode_lens(w)
