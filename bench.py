@@ -90,8 +90,9 @@ def calibrate_copy(mib: int) -> int:
 
 # ---------------------------------------------------------------------------
 def prefill_attention_flops(w) -> float:
-    """4 * h_q * d * sum_p |T(p)|, |T(p)| = min(k, n(p)) * B + (p+1) mod B."""
-    p = np.arange(w.seq, dtype=np.int64)
+    """4 * h_q * d * sum_p |T(p)|, |T(p)| = min(k, n(p)) * B + (p+1) mod B, over the query
+    positions (the last n_q of the sequence for a chunk)."""
+    p = np.arange(w.seq - (w.n_q or w.seq), w.seq, dtype=np.int64)
     n = (p + 1) // w.block
     tsz = np.minimum(w.top_k, n) * w.block + (p + 1) % w.block
     return 4.0 * w.h_q * w.d * float(tsz.sum()) * w.batch
@@ -136,7 +137,8 @@ def setup_prefill(w, dev):
     from block_sparse_attention_37_amd import synth as S
     inps = [S.prefill_inputs(w, seq_id=b) for b in range(w.batch)]
     st = lambda key: torch.stack([S.to_torch(x[key]) for x in inps]).to(dev)
-    plan = Q.PrefillPlan(st("q"), st("k"), st("v"), st("iq"), st("ik"), w.block, w.top_k, w.sm_scale)
+    plan = Q.PrefillPlan(st("q"), st("k"), st("v"), st("iq"), st("ik"), w.block, w.top_k, w.sm_scale,
+                         n_q=w.n_q or None)
     return plan, inps
 
 
@@ -183,7 +185,8 @@ def cpu_baseline(w, inps, lens, budget_s: float):
             t0 = time.perf_counter()
             cmp = O.compress_keys(ik, w.block)
             t_cmp = time.perf_counter() - t0
-            rows = np.random.default_rng(0).permutation(w.seq)
+            nq = w.n_q or w.seq
+            rows = w.seq - nq + np.random.default_rng(0).permutation(nq)
             done, t_rows = 0, 0.0
             for p in rows:
                 t0 = time.perf_counter()
@@ -195,9 +198,9 @@ def cpu_baseline(w, inps, lens, budget_s: float):
                 done += 1
                 if time.perf_counter() - t_start > budget_s:
                     break
-            per_tok = t_rows / done + t_cmp / w.seq
+            per_tok = t_rows / done + t_cmp / nq
             sample = (f"compression of all {w.seq} tokens + selection and attention of {done} "
-                      f"randomly chosen query rows of {w.seq}; tokens/s extrapolated per row")
+                      f"randomly chosen query rows of {nq}; tokens/s extrapolated per row")
             value = 1.0 / per_tok
         else:
             done, t_seq = 0, 0.0
@@ -244,7 +247,7 @@ def main():
     if w.kind == "prefill":
         plan, inps = setup_prefill(w, dev)
         lens = None
-        tokens = w.batch * w.seq
+        tokens = w.batch * (w.n_q or w.seq)  # query tokens processed per step
     else:
         plan, lens = setup_decode(w, dev)
         inps = None
@@ -327,6 +330,8 @@ def main():
            "d_idx": w.d_idx, "graph": bool(args.graph)}
     if w.kind == "prefill":
         cfg["seq"] = w.seq
+        if w.n_q:
+            cfg["n_q"] = w.n_q
     else:
         cfg.update(max_len=w.max_len, kv_len_min=int(lens.min()), kv_len_max=int(lens.max()))
     line = {

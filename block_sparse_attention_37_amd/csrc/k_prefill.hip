@@ -133,7 +133,8 @@ template <int D, int G>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int seq, int h_q, int h_kv, int block, int top_k, float scale_log2,
+    float* __restrict__ lse, int n_q, int kv_len, int h_q, int h_kv, int block, int top_k,
+    float scale_log2,
     int ntiles, int total_wg) {
   constexpr int NT = NW * 64;
   constexpr int PW = 32 / G;       // positions per wave
@@ -163,8 +164,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int tile = ntiles - 1 - logical % ntiles;
   const int g = (logical / ntiles) % h_kv;
   const int b = logical / (ntiles * h_kv);
-  const int p0 = tile * MQ;
-  const int p_hi = min(p0 + MQ, seq) - 1;
+  // query rows q0 .. q0+MQ-1 sit at positions p = p_off + row (bottom-right causal)
+  const int p_off = kv_len - n_q;
+  const int q0 = tile * MQ;
+  const int p0 = p_off + q0;
+  const int p_hi = p_off + min(q0 + MQ, n_q) - 1;
   const int words = (p_hi / block) / 32 + 1;
 
   const int tid = threadIdx.x;
@@ -176,8 +180,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int pos = e / top_k;
     const int p = p0 + pos;
     int j = INT_MAX;
-    if (p < seq) {
-      const int jj = sel[((size_t)b * seq + p) * top_k + (e - pos * top_k)];
+    if (p < kv_len) {
+      const int jj = sel[((size_t)b * n_q + q0 + pos) * top_k + (e - pos * top_k)];
       if (jj >= 0 && jj < (p + 1) / block) j = jj;
     }
     sel_s[e] = j;
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   }
   if (tid < MQ) {
     const int p = p0 + tid;
-    if (p < seq && (p + 1) % block != 0) {
+    if (p < kv_len && (p + 1) % block != 0) {
       const int j = p / block;
       atomicOr(&bm[j >> 5], 1u << (j & 31));
     }
@@ -203,12 +207,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int pos = wave * PW + row / G;
   const int hh = g * G + row % G;
   const int p = p0 + pos;
-  const bool valid_row = p < seq;
+  const bool valid_row = p < kv_len;
   const int own_block = (valid_row && (p + 1) % block != 0) ? p / block : -1;
 
   bf16x8 qreg[NKS];
   {
-    const uint16_t* qp = q + (((size_t)b * seq + (valid_row ? p : 0)) * h_q + hh) * D + half * 8;
+    const uint16_t* qp = q + (((size_t)b * n_q + (valid_row ? p - p_off : 0)) * h_q + hh) * D + half * 8;
 #pragma unroll
     for (int t = 0; t < NKS; ++t) {
       u32x4 w = *reinterpret_cast<const u32x4*>(qp + t * 16);
@@ -229,8 +233,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 
   const int nsub = (block + KC - 1) / KC;
   const uint32_t kv_row = (uint32_t)h_kv * D;  // elements between consecutive tokens
-  const uint16_t* kbase = k + ((size_t)b * seq * h_kv + g) * D;
-  const uint16_t* vbase = v + ((size_t)b * seq * h_kv + g) * D;
+  const uint16_t* kbase = k + ((size_t)b * kv_len * h_kv + g) * D;
+  const uint16_t* vbase = v + ((size_t)b * kv_len * h_kv + g) * D;
 
   // number of chunks the workgroup walks
   int nblk = 0;
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         const int id = wave * KI + i, t = id >> 1, part = id & 1;
         const int r = 32 * part + (lane >> 1);
         const int col = 16 * t + 8 * ((lane & 1) ^ k_unit_swap(r));
-        const uint32_t grow = (uint32_t)min(key0 + r, seq - 1);
+        const uint32_t grow = (uint32_t)min(key0 + r, kv_len - 1);
         global_to_lds16_untracked(kbase + grow * kv_row + col, st0 + t * 2048 + part * 1024);
       }
 #pragma unroll
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         const int id = wave * VI + i, dt = id >> 2, part = id & 3;
         const int r = 16 * part + (lane >> 2);
         const int col = 32 * dt + 8 * ((lane & 3) ^ (2 * v_half_swap(r)));
-        const uint32_t grow = (uint32_t)min(key0 + r, seq - 1);
+        const uint32_t grow = (uint32_t)min(key0 + r, kv_len - 1);
         global_to_lds16_untracked(vbase + grow * kv_row + col, st0 + TILE * 2 + dt * 4096 + part * 1024);
       }
       ++issued;
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     visit(u == 0);
     vis_u = vis;
     key0_u = it_vis.j * block + it_vis.sub * KC;
-    ck_u = min(min(KC, block - it_vis.sub * KC), seq - key0_u);
+    ck_u = min(min(KC, block - it_vis.sub * KC), kv_len - key0_u);
     any_u = __ballot(vis) != 0ull;
   };
   issue_next();
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const float l_tot = pair_sum(l_run);
   if (valid_row) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = out + (((size_t)b * seq + p) * h_q + hh) * D;
+    uint16_t* op = out + (((size_t)b * n_q + (p - p_off)) * h_q + hh) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -490,60 +494,68 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       }
     }
     if (lse && half == 0)
-      lse[((size_t)b * seq + p) * h_q + hh] =
+      lse[((size_t)b * n_q + (p - p_off)) * h_q + hh] =
           l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
   }
 }
 
-bool prefill_bf16_supported(int group, int d, int block, int top_k, int seq) {
+bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len) {
   if (d != 64 && d != 128) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16 && group != 32) return false;
   if (block < 1 || block > 1024 || top_k < 1 || top_k > kMaxTopK) return false;
-  if ((long long)seq * 32 * d >= (1ll << 31)) return false;  // 32-bit offsets within a sequence
+  if ((long long)kv_len * 32 * d >= (1ll << 31)) return false;  // 32-bit offsets within a sequence
   if ((long long)NW * (32 / group) * top_k > kPrefillSelCap) return false;
-  return (seq + block - 1) / block <= kPrefillMaxBlocks;
+  return (kv_len + block - 1) / block <= kPrefillMaxBlocks;
 }
 
 template <int D, int G>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const int32_t* sel,
-                                   void* out, float* lse, int batch, int seq, int h_q, int h_kv,
-                                   int block, int top_k, float sm_scale, hipStream_t stream) {
+                                   void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
+                                   int h_kv, int block, int top_k, float sm_scale,
+                                   hipStream_t stream) {
   constexpr int MQ = NW * (32 / G);
-  const int ntiles = (seq + MQ - 1) / MQ;
+  const int ntiles = (n_q + MQ - 1) / MQ;
   const long long total = (long long)ntiles * h_kv * batch;
   if (total > INT_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3((unsigned)total), dim3(NW * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse, seq,
-                     h_q, h_kv, block, top_k, sm_scale * kLog2e, ntiles, (int)total);
+                     static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse, n_q,
+                     kv_len, h_q, h_kv, block, top_k, sm_scale * kLog2e, ntiles, (int)total);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_prefill_d(int group, const void* q, const void* k, const void* v,
-                                   const int32_t* sel, void* out, float* lse, int batch, int seq,
-                                   int h_q, int h_kv, int block, int top_k, float sm_scale,
-                                   hipStream_t stream) {
+                                   const int32_t* sel, void* out, float* lse, int batch, int n_q,
+                                   int kv_len, int h_q, int h_kv, int block, int top_k,
+                                   float sm_scale, hipStream_t stream) {
+#define QSA_G(g)                                                                             \
+  return launch_prefill_t<D, g>(q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv, block, \
+                                top_k, sm_scale, stream)
   switch (group) {
-    case 1: return launch_prefill_t<D, 1>(q, k, v, sel, out, lse, batch, seq, h_q, h_kv, block, top_k, sm_scale, stream);
-    case 2: return launch_prefill_t<D, 2>(q, k, v, sel, out, lse, batch, seq, h_q, h_kv, block, top_k, sm_scale, stream);
-    case 4: return launch_prefill_t<D, 4>(q, k, v, sel, out, lse, batch, seq, h_q, h_kv, block, top_k, sm_scale, stream);
-    case 8: return launch_prefill_t<D, 8>(q, k, v, sel, out, lse, batch, seq, h_q, h_kv, block, top_k, sm_scale, stream);
-    case 16: return launch_prefill_t<D, 16>(q, k, v, sel, out, lse, batch, seq, h_q, h_kv, block, top_k, sm_scale, stream);
-    case 32: return launch_prefill_t<D, 32>(q, k, v, sel, out, lse, batch, seq, h_q, h_kv, block, top_k, sm_scale, stream);
+    case 1: QSA_G(1);
+    case 2: QSA_G(2);
+    case 4: QSA_G(4);
+    case 8: QSA_G(8);
+    case 16: QSA_G(16);
+    case 32: QSA_G(32);
   }
+#undef QSA_G
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, const int32_t* sel,
-                               void* out, float* lse, int batch, int seq, int h_q, int h_kv,
-                               int d, int block, int top_k, float sm_scale, hipStream_t stream) {
-  if (batch == 0 || seq == 0) return hipSuccess;
+                               void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
+                               int h_kv, int d, int block, int top_k, float sm_scale,
+                               hipStream_t stream) {
+  if (batch == 0 || n_q == 0) return hipSuccess;
   const int group = h_q / h_kv;
   if (d == 128)
-    return launch_prefill_d<128>(group, q, k, v, sel, out, lse, batch, seq, h_q, h_kv, block, top_k, sm_scale, stream);
+    return launch_prefill_d<128>(group, q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv,
+                                 block, top_k, sm_scale, stream);
   if (d == 64)
-    return launch_prefill_d<64>(group, q, k, v, sel, out, lse, batch, seq, h_q, h_kv, block, top_k, sm_scale, stream);
+    return launch_prefill_d<64>(group, q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv,
+                                block, top_k, sm_scale, stream);
   return hipErrorInvalidValue;
 }
 

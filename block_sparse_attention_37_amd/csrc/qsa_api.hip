@@ -141,12 +141,14 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
                   "qsa_index_topk_decode");
 }
 
-qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
-                                   const int32_t* sel, void* out, float* lse, int batch, int seq,
-                                   int h_q, int h_kv, int d, int block, int top_k,
-                                   float sm_scale, qsa_dtype dt, hipStream_t stream) {
+static qsa_status prefill_impl(const char* fn, const void* q, const void* k, const void* v,
+                               const int32_t* sel, void* out, float* lse, int batch, int n_q,
+                               int kv_len, int h_q, int h_kv, int d, int block, int top_k,
+                               float sm_scale, qsa_dtype dt, hipStream_t stream) {
   QSA_REQUIRE(dtype_ok(dt), QSA_ERR_INVALID_ARGUMENT, "dt must be QSA_F32 or QSA_BF16");
-  QSA_REQUIRE(batch >= 0 && seq >= 0, QSA_ERR_INVALID_ARGUMENT, "batch and seq must be >= 0");
+  QSA_REQUIRE(batch >= 0 && n_q >= 0 && kv_len >= 0, QSA_ERR_INVALID_ARGUMENT,
+              "batch, n_q and kv_len must be >= 0");
+  QSA_REQUIRE(n_q <= kv_len, QSA_ERR_INVALID_ARGUMENT, "n_q %d > kv_len %d", n_q, kv_len);
   QSA_REQUIRE(h_q >= 1 && h_kv >= 1 && d >= 1 && block >= 1, QSA_ERR_INVALID_ARGUMENT,
               "h_q, h_kv, d and block must be >= 1");
   QSA_REQUIRE(top_k >= 1, QSA_ERR_INVALID_ARGUMENT, "top_k must be >= 1 (got %d)", top_k);
@@ -157,7 +159,7 @@ qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
   QSA_REQUIRE(top_k <= qsa::kMaxTopK, QSA_ERR_UNSUPPORTED, "top_k %d not supported (<= %d)",
               top_k, qsa::kMaxTopK);
   QSA_REQUIRE(block <= 1024, QSA_ERR_UNSUPPORTED, "block %d not supported (<= 1024)", block);
-  if (batch == 0 || seq == 0) return ok();
+  if (batch == 0 || n_q == 0) return ok();
   QSA_PTR(q, "q");
   QSA_PTR(k, "k");
   QSA_PTR(v, "v");
@@ -165,18 +167,36 @@ qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
   QSA_PTR(out, "out");
   QSA_OPT_PTR(lse, "lse");
   if (dt == QSA_BF16) {
-    QSA_REQUIRE(qsa::prefill_bf16_supported(h_q / h_kv, d, block, top_k, seq), QSA_ERR_UNSUPPORTED,
-                "bf16 prefill not built for group %d, d %d, block %d, top_k %d, seq %d",
-                h_q / h_kv, d, block, top_k, seq);
-    return from_hip(qsa::launch_prefill_bf16(q, k, v, sel, out, lse, batch, seq, h_q, h_kv, d,
-                                             block, top_k, sm_scale, stream),
-                    "qsa_sparse_attn_prefill");
+    QSA_REQUIRE(qsa::prefill_bf16_supported(h_q / h_kv, d, block, top_k, kv_len),
+                QSA_ERR_UNSUPPORTED,
+                "bf16 prefill not built for group %d, d %d, block %d, top_k %d, kv_len %d",
+                h_q / h_kv, d, block, top_k, kv_len);
+    return from_hip(qsa::launch_prefill_bf16(q, k, v, sel, out, lse, batch, n_q, kv_len, h_q,
+                                             h_kv, d, block, top_k, sm_scale, stream),
+                    fn);
   }
   return from_hip(qsa::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                        static_cast<const float*>(v), sel, nullptr,
-                                       static_cast<float*>(out), lse, batch, seq, seq, seq, h_q,
-                                       h_kv, d, block, top_k, sm_scale, stream),
-                  "qsa_sparse_attn_prefill");
+                                       static_cast<float*>(out), lse, batch, n_q, kv_len, kv_len,
+                                       h_q, h_kv, d, block, top_k, sm_scale, stream),
+                  fn);
+}
+
+qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
+                                   const int32_t* sel, void* out, float* lse, int batch, int seq,
+                                   int h_q, int h_kv, int d, int block, int top_k,
+                                   float sm_scale, qsa_dtype dt, hipStream_t stream) {
+  return prefill_impl("qsa_sparse_attn_prefill", q, k, v, sel, out, lse, batch, seq, seq, h_q,
+                      h_kv, d, block, top_k, sm_scale, dt, stream);
+}
+
+qsa_status qsa_sparse_attn_prefill_chunk(const void* q, const void* k, const void* v,
+                                         const int32_t* sel, void* out, float* lse, int batch,
+                                         int n_q, int kv_len, int h_q, int h_kv, int d, int block,
+                                         int top_k, float sm_scale, qsa_dtype dt,
+                                         hipStream_t stream) {
+  return prefill_impl("qsa_sparse_attn_prefill_chunk", q, k, v, sel, out, lse, batch, n_q,
+                      kv_len, h_q, h_kv, d, block, top_k, sm_scale, dt, stream);
 }
 
 qsa_status qsa_sparse_attn_decode_workspace_size(int batch, int h_q, int h_kv, int d, int block,

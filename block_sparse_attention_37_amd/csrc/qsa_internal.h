@@ -33,10 +33,12 @@ hipError_t launch_index_topk_decode(const void* iq, const void* ik, float* cmp,
 // and a bitmap of the blocks it visits in LDS.
 constexpr int kPrefillSelCap = 4096;
 constexpr int kPrefillMaxBlocks = 4096;
-bool prefill_bf16_supported(int group, int d, int block, int top_k, int seq);
+bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len);
+// n_q query rows at positions kv_len - n_q .. kv_len - 1 over kv_len keys.
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, const int32_t* sel,
-                               void* out, float* lse, int batch, int seq, int h_q, int h_kv,
-                               int d, int block, int top_k, float sm_scale, hipStream_t stream);
+                               void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
+                               int h_kv, int d, int block, int top_k, float sm_scale,
+                               hipStream_t stream);
 
 // float32 attention (prefill and decode) on the vector ALUs.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const int32_t* sel,

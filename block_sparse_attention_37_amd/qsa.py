@@ -36,6 +36,8 @@ SIGNATURES = {
     "qsa_index_topk": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "qsa_index_topk_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "qsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "qsa_sparse_attn_prefill_chunk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                           _I, _P]),
     "qsa_sparse_attn_decode_workspace_size": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)]),
     "qsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                     _P, _Z, _I, _P]),
@@ -209,6 +211,33 @@ def sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: 
     return (out, lse) if lse is not None else out
 
 
+def sparse_attn_prefill_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              sel: torch.Tensor, block: int, sm_scale: float | None = None,
+                              return_lse: bool = False, out: torch.Tensor | None = None,
+                              lse: torch.Tensor | None = None):
+    """Attention of the last n_q tokens of each sequence (q [batch, n_q, h_q, d]) over their
+    selected tokens of the whole sequence (k, v [batch, kv_len, h_kv, d]); query i sits at
+    position kv_len - n_q + i."""
+    batch, n_q, h_q, d = q.shape
+    kv_len, h_kv = k.shape[1], k.shape[2]
+    _expect(k, (batch, kv_len, h_kv, d), q.dtype, "k")
+    _expect(v, (batch, kv_len, h_kv, d), q.dtype, "v")
+    top_k = sel.shape[2]
+    _expect(sel, (batch, n_q, top_k), torch.int32, "sel")
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(batch, n_q, h_q, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, (batch, n_q, h_q), torch.float32, "lse")
+    dev = _dev(q, k, v, sel, out, lse)
+    _call("qsa_sparse_attn_prefill_chunk", _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out),
+          _ptr(lse), batch, n_q, kv_len, h_q, h_kv, d, block, top_k, scale, _dt(q), _stream(dev))
+    return (out, lse) if lse is not None else out
+
+
 def decode_workspace_bytes(batch: int, h_q: int, h_kv: int, d: int, block: int, top_k: int) -> int:
     n = ctypes.c_size_t(0)
     _call("qsa_sparse_attn_decode_workspace_size", batch, h_q, h_kv, d, block, top_k, ctypes.byref(n))
@@ -284,26 +313,44 @@ def decode(q, k_cache, v_cache, kv_lens, iq, cmp, block: int, top_k: int,
 # just the C calls (for steady-state loops and HIP graph capture).
 # ---------------------------------------------------------------------------
 class PrefillPlan:
-    """compress -> index/top-k -> sparse attention for fixed prefill tensors."""
+    """compress -> index/top-k -> sparse attention for fixed prefill tensors.  With
+    ``n_q`` the queries are the last n_q tokens of each sequence (chunked prefill onto
+    the cache of the earlier tokens: index with kv_lens = seq, then
+    qsa_sparse_attn_prefill_chunk)."""
 
-    def __init__(self, q, k, v, iq, ik, block: int, top_k: int, sm_scale: float | None = None):
+    def __init__(self, q, k, v, iq, ik, block: int, top_k: int, sm_scale: float | None = None,
+                 n_q: int | None = None):
         batch, seq, h_q, d = q.shape
         h_kv = k.shape[2]
         _, _, h_idx, d_idx = iq.shape
+        chunk = n_q is not None and n_q != seq
+        nq = n_q if chunk else seq
+        if chunk:
+            if not 0 < nq < seq:
+                raise ValueError(f"n_q {nq} must lie in (0, {seq})")
+            q = q[:, seq - nq:].contiguous()
+            iq = iq[:, seq - nq:].contiguous()
         self.block, self.top_k = block, top_k
         dev = _dev(q, k, v, iq, ik)
         self.cmp = torch.zeros(batch, seq // block, d_idx, dtype=torch.float32, device=dev)
-        self.sel = torch.empty(batch, seq, top_k, dtype=torch.int32, device=dev)
+        self.sel = torch.empty(batch, nq, top_k, dtype=torch.int32, device=dev)
         self.out = torch.empty_like(q)
-        self.lse = torch.empty(batch, seq, h_q, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(batch, nq, h_q, dtype=torch.float32, device=dev)
+        self.kv_lens = torch.full((batch,), seq, dtype=torch.int32, device=dev) if chunk else None
         scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
         self._keep = (q, k, v, iq, ik)
         self.dev = dev
         self._compress = (_ptr(ik), None, _ptr(self.cmp), batch, seq, d_idx, block, _dt(ik))
-        self._index = (_ptr(iq), _ptr(self.cmp), None, _ptr(self.sel), None, batch, seq, h_idx,
-                       d_idx, seq // block, block, top_k, _dt(iq))
-        self._attn = (_ptr(q), _ptr(k), _ptr(v), _ptr(self.sel), _ptr(self.out), _ptr(self.lse),
-                      batch, seq, h_q, h_kv, d, block, top_k, scale, _dt(q))
+        self._index = (_ptr(iq), _ptr(self.cmp), _ptr(self.kv_lens), _ptr(self.sel), None, batch,
+                       nq, h_idx, d_idx, seq // block, block, top_k, _dt(iq))
+        if chunk:
+            self._attn_fn = "qsa_sparse_attn_prefill_chunk"
+            self._attn = (_ptr(q), _ptr(k), _ptr(v), _ptr(self.sel), _ptr(self.out), _ptr(self.lse),
+                          batch, nq, seq, h_q, h_kv, d, block, top_k, scale, _dt(q))
+        else:
+            self._attn_fn = "qsa_sparse_attn_prefill"
+            self._attn = (_ptr(q), _ptr(k), _ptr(v), _ptr(self.sel), _ptr(self.out), _ptr(self.lse),
+                          batch, seq, h_q, h_kv, d, block, top_k, scale, _dt(q))
 
     def run_index(self):
         s = _stream(self.dev)  # the current stream at run time (graph capture uses its own)
@@ -311,7 +358,7 @@ class PrefillPlan:
         _call("qsa_index_topk", *self._index, s)
 
     def run_attention(self):
-        _call("qsa_sparse_attn_prefill", *self._attn, _stream(self.dev))
+        _call(self._attn_fn, *self._attn, _stream(self.dev))
 
     def run(self):
         self.run_index()

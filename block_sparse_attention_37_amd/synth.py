@@ -48,6 +48,7 @@ class Workload:
     query_mean: bool = False
     plant_frac: float = 0.0   # fraction of complete blocks planted (seeded choice)
     plant_every: int = 0      # or plant blocks j % plant_every == 0
+    n_q: int = 0              # chunked prefill: the queries are the last n_q tokens (0 = all)
     note: str = field(default="", compare=False)
 
     @property
@@ -75,6 +76,11 @@ WORKLOADS = {
         "long_prefill_bf16_128k", 4, "prefill", "bf16", batch=1, seq=131072 + 77, block=128,
         top_k=64, h_q=32, h_kv=4, d=128, h_idx=16, d_idx=64, query_mean=True, plant_every=32,
         note="1024 complete blocks + 77 trailing; blocks j % 32 == 0 planted (every 4096 tokens)"),
+    "chunk_prefill_bf16_128k": Workload(
+        "chunk_prefill_bf16_128k", 4, "prefill", "bf16", batch=1, seq=131072 + 77, block=128,
+        top_k=64, h_q=32, h_kv=4, d=128, h_idx=16, d_idx=64, query_mean=True, plant_every=32,
+        n_q=4096, note="the last 4096 tokens of the 128k prompt (same inputs) as one chunk "
+                       "over the whole sequence"),
     "long_decode_bf16_b128": Workload(
         "long_decode_bf16_b128", 5, "decode", "bf16", batch=128, max_len=131072,
         len_lo=131072, len_hi=131072, block=128, top_k=64, h_q=32, h_kv=4, d=128, h_idx=16,

@@ -79,8 +79,8 @@ int qsa_version(void);
  *   ik       [batch, max_len, d_idx]  element type dt; the single indexer key head
  *   kv_lens  [batch] int32 or NULL; each value must lie in [0, max_len]
  *   cmp      [batch, max_len / block, d_idx] float32 (output, floor division)
- * Supported: d_idx in {32, 64, 128}, block in [1, 1024].  Accumulation is float32 in
- * token order.
+ * Supported: d_idx in {32, 64, 128}, block in [1, 1024].  Accumulation is float32 in a
+ * fixed order (the same for every call and for qsa_index_topk_decode).
  */
 qsa_status qsa_compress_keys(const void* ik, const int32_t* kv_lens, float* cmp,
                              int batch, int max_len, int d_idx, int block,
@@ -165,14 +165,36 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
  * Invalid: h_q % h_kv != 0.  bf16 computes Q.K^T and P.V on bf16 matrix cores with
  * float32 accumulation and float32 softmax (P rounded to bf16), out rounded to nearest
  * even; f32 computes everything in float32.
- * Supported: d in {64, 128}; bf16 needs h_q / h_kv in {1, 2, 4, 8, 16, 32};
- * top_k <= 256; block in [1, 1024]; (seq + block - 1) / block <= 65536.
+ * Supported: d in {64, 128}; top_k <= 256; block in [1, 1024].  bf16 also needs
+ * G = h_q / h_kv in {1, 2, 4, 8, 16, 32}, (256 / G) * top_k <= 4096 (the selection rows of
+ * a tile of 256 / G positions stay in LDS), (seq + block - 1) / block <= 4096 and
+ * seq * 32 * d < 2^31.
  */
 qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                    const int32_t* sel, void* out, float* lse,
                                    int batch, int seq, int h_q, int h_kv, int d,
                                    int block, int top_k, float sm_scale,
                                    qsa_dtype dt, hipStream_t stream);
+
+/*
+ * Steps 4 + 5, chunked prefill onto an existing cache -- the last n_q tokens of a sequence
+ * of kv_len tokens attend over their selected tokens (Qwen4-Exp, as above; the queries are
+ * the tail of the sequence, so query i sits at position p = kv_len - n_q + i, the same rule
+ * qsa_index_topk applies with kv_lens[b] = kv_len).  With n_q == kv_len this is
+ * qsa_sparse_attn_prefill.
+ *
+ *   q, out   [batch, n_q, h_q, d]     element type dt (out may not alias any input)
+ *   k, v     [batch, kv_len, h_kv, d] element type dt (the whole sequence, cache included)
+ *   sel      [batch, n_q, top_k] int32, as for qsa_sparse_attn_prefill
+ *   lse      [batch, n_q, h_q] float32 output or NULL
+ * Invalid: n_q > kv_len; as qsa_sparse_attn_prefill otherwise.
+ * Supported: as qsa_sparse_attn_prefill with seq = kv_len.
+ */
+qsa_status qsa_sparse_attn_prefill_chunk(const void* q, const void* k, const void* v,
+                                         const int32_t* sel, void* out, float* lse,
+                                         int batch, int n_q, int kv_len, int h_q, int h_kv,
+                                         int d, int block, int top_k, float sm_scale,
+                                         qsa_dtype dt, hipStream_t stream);
 
 /*
  * Bytes of device workspace qsa_sparse_attn_decode needs for these sizes (may be 0).

@@ -114,6 +114,12 @@ def test_prefill_validation(qsa_lib):
     assert call(lse=FAKE + 4) == INVALID
     assert call(h_q=48, h_kv=1) == UNSUPPORTED  # group 48 not built for bf16
     assert call(seq=0) == 0
+    chunk = lambda n_q, kv_len: L.qsa_sparse_attn_prefill_chunk(
+        FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, n_q, kv_len, 8, 2, 128, 16, 4, 0.1, 1, None)
+    assert chunk(200, 100) == INVALID
+    assert "kv_len" in _err()
+    assert chunk(-1, 100) == INVALID
+    assert chunk(0, 100) == 0
 
 
 def test_decode_validation(qsa_lib):

@@ -103,6 +103,48 @@ def test_prefill_edge_shapes(gpu, w):
     check_prefill(w, inp, res)
 
 
+CHUNK_PREFILL = [
+    # (workload over the whole sequence, n_q): the queries are its last n_q tokens
+    (_wl("chunk_g8_d128", seq=300, block=32, top_k=3, h_q=8, h_kv=2, d=128, h_idx=3, d_idx=64,
+         query_mean=True, plant_frac=0.2), 70),
+    (_wl("chunk_g4_d64_one_row", seq=129, block=16, top_k=4, h_q=8, h_kv=2, d=64), 1),
+    (_wl("chunk_g1_block_end", seq=256, block=16, top_k=5, h_q=2, h_kv=2, d=128), 96),
+    (_wl("chunk_g16_all_rows", seq=80, block=16, top_k=2, h_q=16, h_kv=1, d=128), 80),
+    (_wl("chunk_f32", seq=150, block=8, top_k=3, h_q=4, h_kv=2, d=64, dtype="f32"), 41),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_PREFILL, ids=lambda c: c[0].name)
+def test_prefill_chunk(gpu, case):
+    """Chunked prefill: the last n_q tokens over the whole sequence (query i at
+    p = kv_len - n_q + i), selection by qsa_index_topk with kv_lens, attention by
+    qsa_sparse_attn_prefill_chunk; against the oracle row by row."""
+    w, n_q = case
+    say(f"case chunk {w.name} n_q={n_q}")
+    T, B = w.seq, w.block
+    inp = S.prefill_inputs(w)
+    q, k, v = _t(inp["q"], gpu)[None], _t(inp["k"], gpu)[None], _t(inp["v"], gpu)[None]
+    iq, ik = _t(inp["iq"], gpu)[None], _t(inp["ik"], gpu)[None]
+    kvl = torch.tensor([T], dtype=torch.int32, device=gpu)
+    cmp = Q.compress_keys(ik, B)
+    sel = Q.index_topk(iq[:, T - n_q:].contiguous(), cmp, B, w.top_k, kv_lens=kvl)
+    out, lse = Q.sparse_attn_prefill_chunk(q[:, T - n_q:].contiguous(), k, v, sel, B, w.sm_scale,
+                                           return_lse=True)
+    torch.cuda.synchronize()
+    sel_n, out_n, lse_n = sel.cpu().numpy()[0], out.float().cpu().numpy()[0], lse.cpu().numpy()[0]
+    q64, k64, v64 = S.to_f64(inp["q"]), S.to_f64(inp["k"]), S.to_f64(inp["v"])
+    cmp_o = O.compress_keys(S.to_f64(inp["ik"]), B)
+    fails, ties = check_selection(sel_n, S.to_f64(inp["iq"])[T - n_q:], cmp_o, T, B, w.top_k)
+    assert not fails, "\n".join(fails[:5])
+    positions = np.arange(T - n_q, T)
+    out_o, lse_o = O.attend_rows(q64[T - n_q:], k64, v64, sel_n, positions, range(n_q), B,
+                                 w.sm_scale)
+    e_out, e_lse = max_abs(out_n, out_o), max_abs(lse_n, lse_o)
+    say(f"  tie-band rows={ties} out err={e_out:.3g} lse err={e_lse:.3g}")
+    assert e_out <= OUT_ATOL[w.dtype], f"out max-abs error {e_out}"
+    assert e_lse <= LSE_ATOL[w.dtype], f"lse max-abs error {e_lse}"
+
+
 def test_prefill_batch2(gpu):
     w = _wl("batch2", seq=150, block=16, top_k=3, h_q=8, h_kv=2, d=128, batch=2)
     say("case prefill batch2")
@@ -189,6 +231,34 @@ def test_long_prefill_bf16_128k_sampled(gpu):
     att_rows = _stratified_rows(w.seq, w.block, 200, 8)
     att_rows = [r for r in att_rows if r < 64 or r % 3 == 0 or (r + 1) % w.block == 0][:400]
     check_prefill(w, inp, res, rows=att_rows, sel_rows=sel_rows)
+
+
+@pytest.mark.slow
+def test_chunk_prefill_bf16_128k_matches_full(gpu):
+    """The last 4096 tokens of the 128k prompt as one chunk: selections bit-identical to the
+    full prefill's rows, outputs within the bf16 tolerance of them, and a row sample against
+    the oracle."""
+    w = S.WORKLOADS["chunk_prefill_bf16_128k"]
+    T, n_q, B = w.seq, w.n_q, w.block
+    say(f"case {w.name}: generating")
+    inp = S.prefill_inputs(w)
+    st = lambda key: _t(inp[key], gpu)[None]
+    full = Q.PrefillPlan(st("q"), st("k"), st("v"), st("iq"), st("ik"), B, w.top_k, w.sm_scale)
+    full.run()
+    chunk = Q.PrefillPlan(st("q"), st("k"), st("v"), st("iq"), st("ik"), B, w.top_k, w.sm_scale,
+                          n_q=n_q)
+    chunk.run()
+    torch.cuda.synchronize()
+    assert torch.equal(chunk.sel, full.sel[:, T - n_q:])
+    e = (chunk.out.float() - full.out[:, T - n_q:].float()).abs().max().item()
+    assert e <= OUT_ATOL["bf16"], f"chunk vs full prefill: {e}"
+    rows = [0, 1, 127, 2048, n_q - 2, n_q - 1]
+    sel_n = chunk.sel.cpu().numpy()[0]
+    out_o, _ = O.attend_rows(S.to_f64(inp["q"])[T - n_q:], S.to_f64(inp["k"]), S.to_f64(inp["v"]),
+                             sel_n, np.arange(T - n_q, T), rows, B, w.sm_scale)
+    e_o = max_abs(chunk.out.float().cpu().numpy()[0][rows], out_o)
+    say(f"  chunk vs full {e:.3g}, vs oracle {e_o:.3g}")
+    assert e_o <= OUT_ATOL["bf16"]
 
 
 # ---------------------------------------------------------------------------
