@@ -41,6 +41,7 @@ namespace {
 constexpr int KC = 64;   // keys per LDS chunk
 constexpr int NW = 8;    // waves per workgroup
 constexpr int NS = 4;    // LDS stages (chunks in flight + the one being used)
+constexpr int kNoSel = 0xFFFF;  // empty selection slot (block ids stay below kPrefillMaxBlocks)
 
 template <int N>
 struct Int {
@@ -117,14 +118,14 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 
 // LDS layout of one stage (byte offsets), chosen so that every operand read of a lane is
-// one base register plus an immediate and every read is free of bank conflicts:
+// one base register plus an immediate and no read has a bank conflict (both checked with
+// the SQ_LDS_BANK_CONFLICT counter on gfx950 for exactly these lane patterns):
 //  K: D/16 slabs of 16 columns (one per k-step t of S^T = K . Q^T), slab t at t * 2048;
-//     row r at r * 32, its two 16-byte units swapped when bit 2 of r is set (8 lanes of a
-//     ds_read_b128 phase then cover all 32 banks).
+//     row r at r * 32, its two 16-byte units swapped when bit 3 of r is set (with bit 2,
+//     or no swap, the ds_read_b128 of 32 rows takes two passes).
 //  V: D/32 slabs of 32 columns (one per 32-wide d tile of O^T), after the K slabs, slab dt at
-//     dt * 4096; row r at r * 64, its two 32-byte halves swapped when bit 1 of r is set (the
-//     4 rows x 32 bytes of a transpose-read phase then cover all banks).
-__device__ __forceinline__ int k_unit_swap(int r) { return (r >> 2) & 1; }
+//     dt * 4096; row r at r * 64, its two 32-byte halves swapped when bit 1 of r is set.
+__device__ __forceinline__ int k_unit_swap(int r) { return (r >> 3) & 1; }
 __device__ __forceinline__ int v_half_swap(int r) { return (r >> 1) & 1; }
 
 }  // namespace
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // without the compiler draining the load queue before LDS reads.
   constexpr int TILE = KC * D;     // elements of one K (or V) chunk
   __shared__ __attribute__((aligned(16))) uint16_t ring[NS * 2 * TILE];
-  __shared__ int32_t sel_s[kPrefillSelCap];    // [MQ][top_k]
+  __shared__ uint16_t sel_s[kPrefillSelCap];       // [MQ][top_k]; block ids < 4096
   __shared__ uint32_t bm[kPrefillMaxBlocks / 32];  // union bitmap
 
   // ---- which tile: consecutive tiles of one head land on the same XCD (L2); tiles are
@@ -179,10 +180,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   for (int e = tid; e < MQ * top_k; e += NT) {
     const int pos = e / top_k;
     const int p = p0 + pos;
-    int j = INT_MAX;
+    uint16_t j = kNoSel;
     if (p < kv_len) {
       const int jj = sel[((size_t)b * n_q + q0 + pos) * top_k + (e - pos * top_k)];
-      if (jj >= 0 && jj < (p + 1) / block) j = jj;
+      if (jj >= 0 && jj < (p + 1) / block) j = (uint16_t)jj;
     }
     sel_s[e] = j;
   }
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   __syncthreads();
   for (int e = tid; e < MQ * top_k; e += NT) {
     const int j = sel_s[e];
-    if (j != INT_MAX) atomicOr(&bm[j >> 5], 1u << (j & 31));
+    if (j != kNoSel) atomicOr(&bm[j >> 5], 1u << (j & 31));
   }
   if (tid < MQ) {
     const int p = p0 + tid;
@@ -246,8 +247,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   //     physical unit lane % 2) and fetches the logical unit the swap maps there.
   //  V: 4 per slab; piece part of slab dt holds rows 16*part .. +15, lane -> (row lane / 4,
   //     physical unit lane % 4).
-  // Wave w issues K pieces w*KI .. +KI-1 and V pieces w*VI .. +VI-1.  Rows past the chunk
-  // are clamped into the tensor (their keys are masked).
+  // Wave w of group A issues the pieces of waves w and w + NW/2 (K pieces v*KI .. +KI-1
+  // and V pieces v*VI .. +VI-1 of wave v); group B issues none.  Rows past the chunk are
+  // clamped into the tensor (their keys are masked).
   const uint32_t ring_lds = lds_addr(ring);
   ChunkIter it_load{0, (uint32_t)wave_uniform((int)bm[0]), -1, 0};
   next_block(bm, words, it_load);
@@ -258,16 +260,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       const int key0 = it_load.j * block + it_load.sub * KC;
       const uint32_t st0 = ring_lds + (uint32_t)(issued % NS) * (2 * TILE * 2);
 #pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        const int id = wave * KI + i, t = id >> 1, part = id & 1;
+      for (int i = 0; i < 2 * KI; ++i) {
+        const int id = (wave + (i / KI) * (NW / 2)) * KI + i % KI, t = id >> 1, part = id & 1;
         const int r = 32 * part + (lane >> 1);
         const int col = 16 * t + 8 * ((lane & 1) ^ k_unit_swap(r));
         const uint32_t grow = (uint32_t)min(key0 + r, kv_len - 1);
         global_to_lds16_untracked(kbase + grow * kv_row + col, st0 + t * 2048 + part * 1024);
       }
 #pragma unroll
-      for (int i = 0; i < VI; ++i) {
-        const int id = wave * VI + i, dt = id >> 2, part = id & 3;
+      for (int i = 0; i < 2 * VI; ++i) {
+        const int id = (wave + (i / VI) * (NW / 2)) * VI + i % VI, dt = id >> 2, part = id & 3;
         const int r = 16 * part + (lane >> 2);
         const int col = 32 * dt + 8 * ((lane & 3) ^ (2 * v_half_swap(r)));
         const uint32_t grow = (uint32_t)min(key0 + r, kv_len - 1);
@@ -364,14 +366,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     }
     // row max: a tree over the lane's 32 scores (short dependency chains), then the other
     // half of the row on lane ^ 32
-    float t[16];
+    // four chains of three-input maxima (v_max3) over 8 scores each
+    float c[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t[r] = fmaxf(S[0][r], S[1][r]);
-#pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-      for (int r = 0; r < w; ++r) t[r] = fmaxf(t[r], t[r + w]);
-    const float mx = pair_max(t[0]);
+    for (int g = 0; g < 4; ++g) {
+      const int k0 = g >> 1, r0 = 8 * (g & 1);
+      float x = fmaxf(fmaxf(S[k0][r0], S[k0][r0 + 1]), S[k0][r0 + 2]);
+      x = fmaxf(fmaxf(x, S[k0][r0 + 3]), S[k0][r0 + 4]);
+      x = fmaxf(fmaxf(x, S[k0][r0 + 5]), S[k0][r0 + 6]);
+      c[g] = fmaxf(x, S[k0][r0 + 7]);
+    }
+    const float mx = pair_max(fmaxf(fmaxf(fmaxf(c[0], c[1]), c[2]), c[3]));
     // the running max moves only when it grows by more than 8 (log2 units): rare rescales,
     // and every exponent stays <= 8
     const float m_cand = vis ? fmaxf(m_run, mx * scale_log2) : m_run;
@@ -412,7 +417,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // ---- selection walk: visibility of each chunk for this lane's row ----
   ChunkIter it_vis{0, (uint32_t)wave_uniform((int)bm[0]), -1, 0};
   int ptr = 0;
-  int cur_sel = valid_row ? sel_s[pos * top_k] : INT_MAX;
+  int cur_sel = valid_row ? sel_s[pos * top_k] : kNoSel;
   bool vis = false;
   auto visit = [&](bool first) __attribute__((always_inline)) {
     if (first) next_block(bm, words, it_vis);
@@ -421,64 +426,47 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       const bool hit = (cur_sel == it_vis.j);
       if (hit) {
         ++ptr;
-        cur_sel = (ptr < top_k) ? sel_s[pos * top_k + ptr] : INT_MAX;
+        cur_sel = (ptr < top_k) ? sel_s[pos * top_k + ptr] : kNoSel;
       }
       vis = valid_row && (hit || it_vis.j == own_block);
     }
   };
 
   // Chunk u: both groups meet barrier 1 (after chunk u has landed) and barrier 2.
-  //   group A:  barrier 1, MFMA phase u, barrier 2, VALU phase u
+  //   group A:  barrier 1, MFMA phase u, loads of chunk u+2, barrier 2, VALU phase u
   //   group B:  barrier 1, VALU phase u-1, barrier 2, MFMA phase u
-  // followed by the O product of chunk n-1.  The groups run separate loops with the same
-  // barriers, so each loop is straight-line code for the register allocator.
+  // followed by the O product of chunk n-1.  Chunk u+2 takes the stage of chunk u-2,
+  // whose last reader (the O product of group B in its MFMA phase u-1) ended before
+  // barrier 1 of chunk u.  Only group A issues loads, and only after its MFMA phase: the
+  // load queue accepts a chunk's 32 instructions slowly (about 600 cycles per chunk from
+  // L2), and issued by all waves at one barrier they stalled every wave.  Each group
+  // computes the visibility of chunk u+1 at the end of its iteration u, where the LDS
+  // reads of the selection walk complete while it waits at the next barrier.  The groups
+  // run separate loops with the same barriers, so each loop is straight-line code for the
+  // register allocator; each branch ends with its own tail and epilogue, so O needs no
+  // copies where the branches would meet.
   bool vis_prev = false, any_prev = false;
   int key0_prev = 0, ck_prev = 0;
-  auto chunk_begin = [&](int u, bool& vis_u, bool& any_u, int& key0_u, int& ck_u)
-      __attribute__((always_inline)) {
-    // chunk u must have landed; chunk u+1 may stay in flight
-    if (issued > u + 1) wait_vmcnt<DPC>();
+  auto chunk_sync = [&](int u) __attribute__((always_inline)) {
+    // chunk u must have landed (group A waits for its own loads; group B has none); chunk
+    // u+1 may stay in flight
+    if (issued > u + 1) wait_vmcnt<2 * DPC>();
     else wait_vmcnt<0>();
     barrier_no_fence();
-    // every wave is past chunk u-2 (its last reader, the O product of group B, ended
-    // before this barrier): its stage takes chunk u+2
-    issue_next();
+  };
+  auto chunk_visit = [&](int u, bool& vis_u, bool& any_u, int& key0_u, int& ck_u)
+      __attribute__((always_inline)) {
     visit(u == 0);
     vis_u = vis;
     key0_u = it_vis.j * block + it_vis.sub * KC;
     ck_u = min(min(KC, block - it_vis.sub * KC), kv_len - key0_u);
     any_u = __ballot(vis) != 0ull;
   };
-  issue_next();
-  issue_next();
   if (wave < NW / 2) {
-    for (int u = 0; u < n; ++u) {
-      bool vis_u, any_u;
-      int key0_u, ck_u;
-      chunk_begin(u, vis_u, any_u, key0_u, ck_u);
-      mfma_phase(u, any_u, any_prev);
-      barrier_no_fence();
-      if (any_u) valu_phase(vis_u, key0_u, ck_u);
-      any_prev = any_u;
-    }
-  } else {
-    for (int u = 0; u < n; ++u) {
-      bool vis_u, any_u;
-      int key0_u, ck_u;
-      chunk_begin(u, vis_u, any_u, key0_u, ck_u);
-      if (any_prev) valu_phase(vis_prev, key0_prev, ck_prev);
-      barrier_no_fence();
-      mfma_phase(u, any_u, any_prev);
-      vis_prev = vis_u;
-      any_prev = any_u;
-      key0_prev = key0_u;
-      ck_prev = ck_u;
-    }
-    if (any_prev) valu_phase(vis_prev, key0_prev, ck_prev);
+    issue_next();
+    issue_next();
   }
-  if (any_prev) mfma_phase(n, false, true);
-
-  // ---- epilogue ----
+  auto epilogue = [&]() __attribute__((always_inline)) {
   const float l_tot = pair_sum(l_run);
   if (valid_row) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -497,13 +485,49 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
       lse[((size_t)b * n_q + (p - p_off)) * h_q + hh] =
           l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
   }
+  };
+  // visibility of chunk u is computed at the end of iteration u-1, where its LDS reads
+  // complete during the barrier wait
+  bool vis_c, any_c;
+  int key0_c, ck_c;
+  if (n > 0) chunk_visit(0, vis_c, any_c, key0_c, ck_c);
+  if (wave < NW / 2) {
+    for (int u = 0; u < n; ++u) {
+      chunk_sync(u);
+      mfma_phase(u, any_c, any_prev);
+      issue_next();
+      barrier_no_fence();
+      if (any_c) valu_phase(vis_c, key0_c, ck_c);
+      any_prev = any_c;
+      if (u + 1 < n) chunk_visit(u + 1, vis_c, any_c, key0_c, ck_c);
+    }
+    if (any_prev) mfma_phase(n, false, true);
+    epilogue();
+  } else {
+    for (int u = 0; u < n; ++u) {
+      chunk_sync(u);
+      if (any_prev) valu_phase(vis_prev, key0_prev, ck_prev);
+      barrier_no_fence();
+      mfma_phase(u, any_c, any_prev);
+      vis_prev = vis_c;
+      any_prev = any_c;
+      key0_prev = key0_c;
+      ck_prev = ck_c;
+      if (u + 1 < n) chunk_visit(u + 1, vis_c, any_c, key0_c, ck_c);
+    }
+    if (any_prev) valu_phase(vis_prev, key0_prev, ck_prev);
+    if (any_prev) mfma_phase(n, false, true);
+    epilogue();
+  }
+
 }
 
-bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len) {
+bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len, int h_kv) {
   if (d != 64 && d != 128) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16 && group != 32) return false;
   if (block < 1 || block > 1024 || top_k < 1 || top_k > kMaxTopK) return false;
-  if ((long long)kv_len * 32 * d >= (1ll << 31)) return false;  // 32-bit offsets within a sequence
+  // element offsets of K / V rows within one sequence are 32-bit
+  if ((long long)kv_len * h_kv * d >= (1ll << 32)) return false;
   if ((long long)NW * (32 / group) * top_k > kPrefillSelCap) return false;
   return (kv_len + block - 1) / block <= kPrefillMaxBlocks;
 }

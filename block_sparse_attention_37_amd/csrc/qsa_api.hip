@@ -167,10 +167,10 @@ static qsa_status prefill_impl(const char* fn, const void* q, const void* k, con
   QSA_PTR(out, "out");
   QSA_OPT_PTR(lse, "lse");
   if (dt == QSA_BF16) {
-    QSA_REQUIRE(qsa::prefill_bf16_supported(h_q / h_kv, d, block, top_k, kv_len),
+    QSA_REQUIRE(qsa::prefill_bf16_supported(h_q / h_kv, d, block, top_k, kv_len, h_kv),
                 QSA_ERR_UNSUPPORTED,
-                "bf16 prefill not built for group %d, d %d, block %d, top_k %d, kv_len %d",
-                h_q / h_kv, d, block, top_k, kv_len);
+                "bf16 prefill not built for group %d, d %d, block %d, top_k %d, kv_len %d, "
+                "h_kv %d", h_q / h_kv, d, block, top_k, kv_len, h_kv);
     return from_hip(qsa::launch_prefill_bf16(q, k, v, sel, out, lse, batch, n_q, kv_len, h_q,
                                              h_kv, d, block, top_k, sm_scale, stream),
                     fn);

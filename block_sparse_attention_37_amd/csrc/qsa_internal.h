@@ -31,9 +31,9 @@ hipError_t launch_index_topk_decode(const void* iq, const void* ik, float* cmp,
 // bf16 prefill on matrix cores.  Returns hipErrorInvalidValue for shapes it is not built for.
 // A workgroup keeps the selection rows of its query positions (positions x top_k entries)
 // and a bitmap of the blocks it visits in LDS.
-constexpr int kPrefillSelCap = 4096;
+constexpr int kPrefillSelCap = 8192;
 constexpr int kPrefillMaxBlocks = 4096;
-bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len);
+bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len, int h_kv);
 // n_q query rows at positions kv_len - n_q .. kv_len - 1 over kv_len keys.
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, const int32_t* sel,
                                void* out, float* lse, int batch, int n_q, int kv_len, int h_q,

@@ -166,9 +166,9 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
  * float32 accumulation and float32 softmax (P rounded to bf16), out rounded to nearest
  * even; f32 computes everything in float32.
  * Supported: d in {64, 128}; top_k <= 256; block in [1, 1024].  bf16 also needs
- * G = h_q / h_kv in {1, 2, 4, 8, 16, 32}, (256 / G) * top_k <= 4096 (the selection rows of
+ * G = h_q / h_kv in {1, 2, 4, 8, 16, 32}, (256 / G) * top_k <= 8192 (the selection rows of
  * a tile of 256 / G positions stay in LDS), (seq + block - 1) / block <= 4096 and
- * seq * 32 * d < 2^31.
+ * seq * h_kv * d < 2^32.
  */
 qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                    const int32_t* sel, void* out, float* lse,
