@@ -316,7 +316,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = load_traffic(w.name)
     # the attention call: one kernel for prefill; split kernel + merge kernel for decode
-    roof["kernel"] = ("qsa::prefill_bf16_kernel" if w.kind == "prefill"
+    roof["kernel"] = (("qsa::prefill_bf16_rt_kernel" if w.d == 256 else "qsa::prefill_bf16_kernel")
+                      if w.kind == "prefill"
                       else "qsa::decode_bf16_kernel + qsa::decode_merge_kernel")
     roof["algorithmic_per_launch"] = work
     roof["kernel_ms"] = round(att_ms, 5)

@@ -21,8 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
 
-SOURCES = ["qsa_api.hip", "k_compress.hip", "k_index.hip", "k_prefill.hip", "k_decode.hip",
-           "k_attn_f32.hip"]
+SOURCES = ["qsa_api.hip", "k_compress.hip", "k_index.hip", "k_prefill.hip", "k_prefill_rt.hip",
+           "k_decode.hip", "k_attn_f32.hip"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

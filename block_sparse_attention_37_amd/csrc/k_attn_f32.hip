@@ -118,6 +118,7 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const
   return hipGetLastError()
   if (d == 64) { QSA_F32(64); }
   if (d == 128) { QSA_F32(128); }
+  if (d == 256) { QSA_F32(256); }
 #undef QSA_F32
   return hipErrorInvalidValue;
 }

@@ -32,7 +32,12 @@ namespace qsa {
 
 namespace {
 constexpr int KC = 64;  // keys per chunk
-constexpr int NS = 4;   // LDS stages
+
+// LDS stages: four at D <= 128 (128 KB); two at D = 256, where a stage alone is 64 KB.
+template <int D>
+struct DecodeStages {
+  static constexpr int value = D >= 256 ? 2 : 4;
+};
 
 __device__ __forceinline__ f32x4 mfma16x16x16_bf16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<s16x4>(a), bitcast<s16x4>(b), c, 0, 0, 0);
@@ -57,7 +62,9 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(
   constexpr int RPI = 64 / NU;    // rows per LDS-direct instruction (1 KB)
   constexpr int KI = KC / 4 / RPI;  // instructions per wave per K (or V) chunk: 16 rows each
   constexpr int DPC = 2 * KI;     // LDS-direct instructions per wave per chunk
+  constexpr int NS = DecodeStages<D>::value;
   static_assert(2 * DPC < 64, "vmcnt range");
+  static_assert(4 * D * 16 * 4 <= NS * 2 * KC * D * 2, "the wave merge reuses the ring");
 
   __shared__ __attribute__((aligned(16))) uint16_t ring[NS * 2 * TILE];
   __shared__ int32_t list[kMaxTopK];
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 }
 
 bool decode_bf16_supported(int group, int d, int block, int top_k) {
-  if (d != 64 && d != 128) return false;
+  if (d != 64 && d != 128 && d != 256) return false;
   if (group < 1 || group > 16) return false;
   return block >= 1 && block <= 1024 && top_k >= 1 && top_k <= kMaxTopK;
 }
@@ -363,6 +370,9 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
                               int top_k, float sm_scale, void* workspace, int nsplit,
                               hipStream_t stream) {
   if (batch == 0) return hipSuccess;
+  if (d == 256)
+    return launch_decode_t<256>(q, k_cache, v_cache, kv_lens, sel, out, lse, batch, max_len, h_q,
+                                h_kv, block, top_k, sm_scale, workspace, nsplit, stream);
   if (d == 128)
     return launch_decode_t<128>(q, k_cache, v_cache, kv_lens, sel, out, lse, batch, max_len, h_q,
                                 h_kv, block, top_k, sm_scale, workspace, nsplit, stream);

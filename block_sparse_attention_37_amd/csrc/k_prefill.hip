@@ -29,6 +29,7 @@
 //   * Online softmax in base 2 with the scale folded into one FMA per score; the running
 //     max is raised only when it grows by more than 8 (log2 units), so rescaling the
 //     accumulators is rare and every exponent stays <= 8.
+#include "prefill_common.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -42,80 +43,6 @@ constexpr int KC = 64;   // keys per LDS chunk
 constexpr int NW = 8;    // waves per workgroup
 constexpr int NS = 4;    // LDS stages (chunks in flight + the one being used)
 constexpr int kNoSel = 0xFFFF;  // empty selection slot (block ids stay below kPrefillMaxBlocks)
-
-template <int N>
-struct Int {
-  static constexpr int value = N;
-};
-
-struct ChunkIter {
-  int wi;         // bitmap word index
-  uint32_t bits;  // remaining bits of that word
-  int j;          // current block
-  int sub;        // 64-key sub-chunk inside the block
-};
-
-// The bitmap is the same for every lane: its words are made wave-uniform so the walk runs
-// on the scalar unit.
-__device__ __forceinline__ bool next_block(const uint32_t* bm, int words, ChunkIter& it) {
-  while (it.bits == 0u) {
-    if (++it.wi >= words) return false;
-    it.bits = (uint32_t)wave_uniform((int)bm[it.wi]);
-  }
-  const int t = __builtin_ctz(it.bits);
-  it.bits &= it.bits - 1u;
-  it.j = it.wi * 32 + t;
-  it.sub = 0;
-  return true;
-}
-
-__device__ __forceinline__ bool advance(const uint32_t* bm, int words, int nsub, ChunkIter& it) {
-  if (it.sub + 1 < nsub) {
-    ++it.sub;
-    return true;
-  }
-  return next_block(bm, words, it);
-}
-
-// Instruction-order hints for the scheduler (no effect on results): mask selects the
-// instruction class (0x8 MFMA, 0x100 LDS read), n how many of them come next.
-template <int MASK, int N>
-__device__ __forceinline__ void sched_group() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
-#endif
-}
-constexpr int kSchedMfma = 0x8;
-constexpr int kSchedDsRead = 0x100;
-constexpr int kReadAhead = 4;  // LDS operand reads issued ahead of their MFMA (measured best)
-
-// Issue priority of this wave among the waves of its SIMD (s_setprio).
-template <int P>
-__device__ __forceinline__ void set_wave_priority() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_s_setprio(P);
-#endif
-}
-
-// max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap leaves each lane with
-// its own value and its partner's, in some order, which max and sum do not care about.
-__device__ __forceinline__ float pair_max(float x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-#else
-  return x;
-#endif
-}
-__device__ __forceinline__ float pair_sum(float x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-#else
-  return x;
-#endif
-}
-
 
 // LDS layout of one stage (byte offsets), chosen so that every operand read of a lane is
 // one base register plus an immediate and no read has a bank conflict (both checked with
@@ -523,6 +450,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 }
 
 bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len, int h_kv) {
+  if (d == 256) return prefill_bf16_rt_supported(group, d, block, top_k, kv_len, h_kv);
   if (d != 64 && d != 128) return false;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16 && group != 32) return false;
   if (block < 1 || block > 1024 || top_k < 1 || top_k > kMaxTopK) return false;
@@ -574,6 +502,9 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, cons
                                hipStream_t stream) {
   if (batch == 0 || n_q == 0) return hipSuccess;
   const int group = h_q / h_kv;
+  if (d == 256)
+    return launch_prefill_bf16_rt(q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv, d, block,
+                                  top_k, sm_scale, stream);
   if (d == 128)
     return launch_prefill_d<128>(group, q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv,
                                  block, top_k, sm_scale, stream);

@@ -1,0 +1,101 @@
+// Pieces shared by the two block-sparse prefill kernels (32-row waves for head dims 64
+// and 128, 16-row tiles for 256): the walk over the union bitmap of visited blocks,
+// scheduling hints, wave priority and cross-lane reductions of one query row.
+#pragma once
+
+#include "qsa_device.h"
+
+namespace qsa {
+namespace {
+
+struct ChunkIter {
+  int wi;         // bitmap word index
+  uint32_t bits;  // remaining bits of that word
+  int j;          // current block
+  int sub;        // sub-chunk of the block (chunk = the kernel's keys per LDS stage)
+};
+
+// The bitmap is the same for every lane: its words are made wave-uniform so the walk runs
+// on the scalar unit.
+__device__ __forceinline__ bool next_block(const uint32_t* bm, int words, ChunkIter& it) {
+  while (it.bits == 0u) {
+    if (++it.wi >= words) return false;
+    it.bits = (uint32_t)wave_uniform((int)bm[it.wi]);
+  }
+  const int t = __builtin_ctz(it.bits);
+  it.bits &= it.bits - 1u;
+  it.j = it.wi * 32 + t;
+  it.sub = 0;
+  return true;
+}
+
+__device__ __forceinline__ bool advance(const uint32_t* bm, int words, int nsub, ChunkIter& it) {
+  if (it.sub + 1 < nsub) {
+    ++it.sub;
+    return true;
+  }
+  return next_block(bm, words, it);
+}
+
+// Instruction-order hints for the scheduler (no effect on results): mask selects the
+// instruction class (0x8 MFMA, 0x100 LDS read), n how many of them come next.
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+#endif
+}
+constexpr int kSchedMfma = 0x8;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kReadAhead = 4;  // LDS operand reads issued ahead of their MFMA (measured best
+                               // for the 32-row kernel)
+
+// Issue priority of this wave among the waves of its SIMD (s_setprio).
+template <int P>
+__device__ __forceinline__ void set_wave_priority() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_setprio(P);
+#endif
+}
+
+// max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap leaves each lane with
+// its own value and its partner's, in some order, which max and sum do not care about.
+__device__ __forceinline__ float pair_max(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+#else
+  return x;
+#endif
+}
+__device__ __forceinline__ float pair_sum(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+#else
+  return x;
+#endif
+}
+
+// max / sum of x over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 4-key groups of
+// one query row in a 16x16 MFMA tile): v_permlane16_swap pairs l with l ^ 16 the way
+// v_permlane32_swap pairs l with l ^ 32.
+__device__ __forceinline__ float quad_max(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return pair_max(fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+#else
+  return x;
+#endif
+}
+__device__ __forceinline__ float quad_sum(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return pair_sum(__uint_as_float(a[0]) + __uint_as_float(a[1]));
+#else
+  return x;
+#endif
+}
+
+}  // namespace
+}  // namespace qsa

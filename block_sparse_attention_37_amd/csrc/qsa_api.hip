@@ -155,7 +155,8 @@ static qsa_status prefill_impl(const char* fn, const void* q, const void* k, con
   QSA_REQUIRE(h_q % h_kv == 0, QSA_ERR_INVALID_ARGUMENT, "h_q %d is not a multiple of h_kv %d",
               h_q, h_kv);
   QSA_REQUIRE(std::isfinite(sm_scale), QSA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
-  QSA_REQUIRE(d == 64 || d == 128, QSA_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", d);
+  QSA_REQUIRE(d == 64 || d == 128 || d == 256, QSA_ERR_UNSUPPORTED,
+              "head dim %d not supported (64, 128, 256)", d);
   QSA_REQUIRE(top_k <= qsa::kMaxTopK, QSA_ERR_UNSUPPORTED, "top_k %d not supported (<= %d)",
               top_k, qsa::kMaxTopK);
   QSA_REQUIRE(block <= 1024, QSA_ERR_UNSUPPORTED, "block %d not supported (<= 1024)", block);
@@ -223,7 +224,8 @@ qsa_status qsa_sparse_attn_decode(const void* q, const void* k_cache, const void
   QSA_REQUIRE(h_q % h_kv == 0, QSA_ERR_INVALID_ARGUMENT, "h_q %d is not a multiple of h_kv %d",
               h_q, h_kv);
   QSA_REQUIRE(std::isfinite(sm_scale), QSA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
-  QSA_REQUIRE(d == 64 || d == 128, QSA_ERR_UNSUPPORTED, "head dim %d not supported (64, 128)", d);
+  QSA_REQUIRE(d == 64 || d == 128 || d == 256, QSA_ERR_UNSUPPORTED,
+              "head dim %d not supported (64, 128, 256)", d);
   QSA_REQUIRE(top_k <= qsa::kMaxTopK, QSA_ERR_UNSUPPORTED, "top_k %d not supported (<= %d)",
               top_k, qsa::kMaxTopK);
   QSA_REQUIRE(block <= 1024, QSA_ERR_UNSUPPORTED, "block %d not supported (<= 1024)", block);

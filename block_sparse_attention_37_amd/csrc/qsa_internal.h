@@ -39,6 +39,13 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, cons
                                void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
                                int h_kv, int d, int block, int top_k, float sm_scale,
                                hipStream_t stream);
+// The head-dim-256 instance (16-row tiles, 32-key chunks); launch_prefill_bf16 and
+// prefill_bf16_supported route d = 256 here.
+bool prefill_bf16_rt_supported(int group, int d, int block, int top_k, int kv_len, int h_kv);
+hipError_t launch_prefill_bf16_rt(const void* q, const void* k, const void* v, const int32_t* sel,
+                                  void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
+                                  int h_kv, int d, int block, int top_k, float sm_scale,
+                                  hipStream_t stream);
 
 // float32 attention (prefill and decode) on the vector ALUs.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const int32_t* sel,

@@ -85,6 +85,15 @@ WORKLOADS = {
         "long_decode_bf16_b128", 5, "decode", "bf16", batch=128, max_len=131072,
         len_lo=131072, len_hi=131072, block=128, top_k=64, h_q=32, h_kv=4, d=128, h_idx=16,
         d_idx=64, note="context 131072 each (1024 blocks, empty trailing part)"),
+    # the model page's default attention shape: 16 query heads over 2 KV heads of dim 256
+    "prefill_bf16_d256_32k": Workload(
+        "prefill_bf16_d256_32k", 6, "prefill", "bf16", batch=1, seq=32768 + 45, block=128,
+        top_k=32, h_q=16, h_kv=2, d=256, h_idx=8, d_idx=64, query_mean=True, plant_every=16,
+        note="head dim 256, 16/2 heads; 256 complete blocks + 45 trailing"),
+    "decode_bf16_d256_b64": Workload(
+        "decode_bf16_d256_b64", 7, "decode", "bf16", batch=64, max_len=32768, len_lo=8192,
+        len_hi=32768, block=64, top_k=32, h_q=16, h_kv=2, d=256, h_idx=8, d_idx=64,
+        note="head dim 256, 16/2 heads; context lengths uniform in [8192, 32768]"),
 }
 
 

@@ -165,10 +165,11 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
  * Invalid: h_q % h_kv != 0.  bf16 computes Q.K^T and P.V on bf16 matrix cores with
  * float32 accumulation and float32 softmax (P rounded to bf16), out rounded to nearest
  * even; f32 computes everything in float32.
- * Supported: d in {64, 128}; top_k <= 256; block in [1, 1024].  bf16 also needs
- * G = h_q / h_kv in {1, 2, 4, 8, 16, 32}, (256 / G) * top_k <= 8192 (the selection rows of
- * a tile of 256 / G positions stay in LDS), (seq + block - 1) / block <= 4096 and
- * seq * h_kv * d < 2^32.
+ * Supported: d in {64, 128, 256} (256: the model page's default attention shape);
+ * top_k <= 256; block in [1, 1024].  bf16 also needs G = h_q / h_kv in {1, 2, 4, 8, 16, 32},
+ * T * top_k <= 8192 where T = 256 / G positions per tile for d <= 128 and
+ * T = 128 / G (8 when G = 32) for d = 256 (the selection rows of a tile stay in LDS),
+ * (seq + block - 1) / block <= 4096 and seq * h_kv * d < 2^32.
  */
 qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                    const int32_t* sel, void* out, float* lse,
@@ -222,7 +223,7 @@ qsa_status qsa_sparse_attn_decode_workspace_size(int batch, int h_q, int h_kv, i
  *                     allowed when that size is 0); contents need no initialization and
  *                     are scratch: two calls in flight at once must not share it
  * Invalid: h_q % h_kv != 0, workspace_bytes too small.
- * Supported: d in {64, 128}; bf16 needs h_q / h_kv in {1, 2, 4, 8, 16}; top_k <= 256;
+ * Supported: d in {64, 128, 256}; bf16 needs h_q / h_kv in {1, 2, 4, 8, 16}; top_k <= 256;
  * block in [1, 1024].
  */
 qsa_status qsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,

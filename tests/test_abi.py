@@ -114,6 +114,11 @@ def test_prefill_validation(qsa_lib):
     assert call(lse=FAKE + 4) == INVALID
     assert call(h_q=48, h_kv=1) == UNSUPPORTED  # group 48 not built for bf16
     assert call(seq=0) == 0
+    # head dim 256: accepted; its tile of 128 / G positions caps top_k at 64 when G = 1
+    assert call(d=256, seq=0) == 0
+    assert call(d=192) == UNSUPPORTED
+    assert call(d=256, h_q=2, h_kv=2, top_k=65) == UNSUPPORTED
+    assert call(d=128, h_q=2, h_kv=2, top_k=65) == UNSUPPORTED  # 256 positions x 65 > 8192
     chunk = lambda n_q, kv_len: L.qsa_sparse_attn_prefill_chunk(
         FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, n_q, kv_len, 8, 2, 128, 16, 4, 0.1, 1, None)
     assert chunk(200, 100) == INVALID
@@ -145,6 +150,8 @@ def test_decode_validation(qsa_lib):
     assert call(h_q=30) == INVALID
     assert call(h_q=64, h_kv=2) == UNSUPPORTED  # group 32 > 16 not built for bf16 decode
     assert call(batch=0) == 0
+    assert call(d=256, batch=0) == 0
+    assert call(d=192) == UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():

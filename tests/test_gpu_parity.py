@@ -92,6 +92,13 @@ EDGE_PREFILL = [
         d_idx=64, query_mean=True, plant_frac=0.1),
     _wl("f32_small", seq=77, block=8, top_k=3, h_q=4, h_kv=2, d=64, dtype="f32"),
     _wl("f32_d128", seq=40, block=16, top_k=1, h_q=2, h_kv=1, d=128, dtype="f32"),
+    # head dim 256 (the model page's default attention shape: 16 query / 2 KV heads)
+    _wl("d256_default_heads", seq=300, block=32, top_k=3, h_q=16, h_kv=2, d=256, h_idx=4,
+        d_idx=64, query_mean=True, plant_frac=0.1),
+    _wl("d256_g1", seq=70, block=16, top_k=2, h_q=2, h_kv=2, d=256),
+    _wl("d256_g32", seq=50, block=16, top_k=2, h_q=32, h_kv=1, d=256),
+    _wl("d256_g16_block100", seq=260, block=100, top_k=1, h_q=16, h_kv=1, d=256),
+    _wl("f32_d256", seq=40, block=16, top_k=2, h_q=4, h_kv=2, d=256, dtype="f32"),
 ]
 
 
@@ -111,6 +118,7 @@ CHUNK_PREFILL = [
     (_wl("chunk_g1_block_end", seq=256, block=16, top_k=5, h_q=2, h_kv=2, d=128), 96),
     (_wl("chunk_g16_all_rows", seq=80, block=16, top_k=2, h_q=16, h_kv=1, d=128), 80),
     (_wl("chunk_f32", seq=150, block=8, top_k=3, h_q=4, h_kv=2, d=64, dtype="f32"), 41),
+    (_wl("chunk_d256", seq=200, block=32, top_k=3, h_q=16, h_kv=2, d=256, h_idx=3, d_idx=64), 50),
 ]
 
 
@@ -234,6 +242,20 @@ def test_long_prefill_bf16_128k_sampled(gpu):
 
 
 @pytest.mark.slow
+def test_prefill_bf16_d256_32k_sampled(gpu):
+    """Head dim 256 (16/2 heads) at 32k: selection on a stratified sample, attention on
+    fewer rows, against the oracle."""
+    w = S.WORKLOADS["prefill_bf16_d256_32k"]
+    say(f"case {w.name}: generating inputs")
+    inp = S.prefill_inputs(w)
+    say("  running GPU path")
+    res = gpu_prefill(w, [inp], gpu)
+    sel_rows = _stratified_rows(w.seq, w.block, 3000, 9)
+    att_rows = _stratified_rows(w.seq, w.block, 150, 10)[:300]
+    check_prefill(w, inp, res, rows=att_rows, sel_rows=sel_rows)
+
+
+@pytest.mark.slow
 def test_chunk_prefill_bf16_128k_matches_full(gpu):
     """The last 4096 tokens of the 128k prompt as one chunk: selections bit-identical to the
     full prefill's rows, outputs within the bf16 tolerance of them, and a row sample against
@@ -341,6 +363,12 @@ EDGE_DECODE = [
      [5, 100, 200]),
     (_dw("wide_split", batch=1, max_len=8192, block=64, top_k=64, h_q=8, h_kv=1, d=128),
      [8000]),
+    (_dw("d256_default_heads", batch=4, max_len=600, block=32, top_k=4, h_q=16, h_kv=2, d=256),
+     [1, 33, 300, 600]),
+    (_dw("d256_wide_split", batch=1, max_len=4096, block=64, top_k=32, h_q=16, h_kv=2, d=256),
+     [4000]),
+    (_dw("f32_d256", batch=2, max_len=100, block=16, top_k=2, h_q=4, h_kv=2, d=256, dtype="f32"),
+     [50, 100]),
 ]
 
 
@@ -436,6 +464,18 @@ def test_decode_bf16_b64_full(gpu):
     lens = S.decode_lens(w)
     say(f"case {w.name}: generating")
     *tensors, keep = gpu_decode_setup(w, lens, gpu)
+    res = gpu_decode(w, lens, tensors)
+    check_decode(w, lens, res, keep)
+
+
+def test_decode_bf16_d256_b64_sampled(gpu):
+    """Head dim 256 (16/2 heads), batch 64 at 8k..32k context: every sequence's selection
+    and attention on a sample of sequences against the oracle."""
+    w = S.WORKLOADS["decode_bf16_d256_b64"]
+    lens = S.decode_lens(w)
+    seqs = {0, 1, 17, 31, 32, 50, 62, 63}
+    say(f"case {w.name}: generating")
+    *tensors, keep = gpu_decode_setup(w, lens, gpu, seqs=seqs)
     res = gpu_decode(w, lens, tensors)
     check_decode(w, lens, res, keep)
 
