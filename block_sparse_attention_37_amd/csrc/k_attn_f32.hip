@@ -39,7 +39,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   const int lane = threadIdx.x;
   const int g = h / (h_q / h_kv);
   int len = kv_lens ? kv_lens[b] : seq_fixed;
-  len = len > kv_stride_len ? kv_stride_len : len;
+  len = len < 0 ? 0 : (len > kv_stride_len ? kv_stride_len : len);
   const int p = len - n_q + i;
   const size_t qo = (((size_t)b * n_q + i) * h_q + h) * D;
   for (int d = lane; d < D; d += 64) qs[d] = q[qo + d];

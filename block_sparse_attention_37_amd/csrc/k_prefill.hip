@@ -61,9 +61,9 @@ template <int D, int G>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int n_q, int kv_len, int h_q, int h_kv, int block, int top_k,
-    float scale_log2,
-    int ntiles, int total_wg) {
+    float* __restrict__ lse, int n_q, int kv_len_all, int h_q, int h_kv, int block, int top_k,
+    float scale_log2, int ntiles, int total_wg, const int32_t* __restrict__ kv_lens,
+    int kv_stride) {
   constexpr int NT = NW * 64;
   constexpr int PW = 32 / G;       // positions per wave
   constexpr int MQ = NW * PW;      // positions per workgroup
@@ -92,12 +92,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int tile = ntiles - 1 - logical % ntiles;
   const int g = (logical / ntiles) % h_kv;
   const int b = logical / (ntiles * h_kv);
-  // query rows q0 .. q0+MQ-1 sit at positions p = p_off + row (bottom-right causal)
+  // keys of this sequence: kv_lens[b] (clamped to the kv_stride rows of its K/V slab), or
+  // the common length
+  const int kv_len = kv_lens ? min(max(kv_lens[b], 0), kv_stride) : kv_len_all;
+  // query rows q0 .. q0+MQ-1 sit at positions p = p_off + row (bottom-right causal); rows
+  // with p < 0 are padding (a sequence shorter than n_q)
   const int p_off = kv_len - n_q;
   const int q0 = tile * MQ;
   const int p0 = p_off + q0;
   const int p_hi = p_off + min(q0 + MQ, n_q) - 1;
-  const int words = (p_hi / block) / 32 + 1;
+  const int words = p_hi >= 0 ? (p_hi / block) / 32 + 1 : 0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,13 +112,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int pos = e / top_k;
     const int p = p0 + pos;
     uint16_t j = kNoSel;
-    if (p < kv_len) {
+    if (p >= 0 && p < kv_len) {
       const int jj = sel[((size_t)b * n_q + q0 + pos) * top_k + (e - pos * top_k)];
       if (jj >= 0 && jj < (p + 1) / block) j = (uint16_t)jj;
     }
     sel_s[e] = j;
   }
-  for (int w = tid; w < words; w += NT) bm[w] = 0u;
+  for (int w = tid; w < max(words, 1); w += NT) bm[w] = 0u;
   __syncthreads();
   for (int e = tid; e < MQ * top_k; e += NT) {
     const int j = sel_s[e];
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   }
   if (tid < MQ) {
     const int p = p0 + tid;
-    if (p < kv_len && (p + 1) % block != 0) {
+    if (p >= 0 && p < kv_len && (p + 1) % block != 0) {
       const int j = p / block;
       atomicOr(&bm[j >> 5], 1u << (j & 31));
     }
@@ -135,7 +139,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int pos = wave * PW + row / G;
   const int hh = g * G + row % G;
   const int p = p0 + pos;
-  const bool valid_row = p < kv_len;
+  const bool valid_row = p >= 0 && p < kv_len;
+  const bool pad_row = p < 0 && q0 + pos < n_q;  // a padding row: zero output
   const int own_block = (valid_row && (p + 1) % block != 0) ? p / block : -1;
 
   bf16x8 qreg[NKS];
@@ -161,8 +166,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 
   const int nsub = (block + KC - 1) / KC;
   const uint32_t kv_row = (uint32_t)h_kv * D;  // elements between consecutive tokens
-  const uint16_t* kbase = k + ((size_t)b * kv_len * h_kv + g) * D;
-  const uint16_t* vbase = v + ((size_t)b * kv_len * h_kv + g) * D;
+  const uint16_t* kbase = k + ((size_t)b * kv_stride * h_kv + g) * D;
+  const uint16_t* vbase = v + ((size_t)b * kv_stride * h_kv + g) * D;
 
   // number of chunks the workgroup walks
   int nblk = 0;
@@ -394,24 +399,24 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     issue_next();
   }
   auto epilogue = [&]() __attribute__((always_inline)) {
-  const float l_tot = pair_sum(l_run);
-  if (valid_row) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = out + (((size_t)b * n_q + (p - p_off)) * h_q + hh) * D;
+    const float l_tot = pair_sum(l_run);
+    if (valid_row || pad_row) {
+      const float inv = (valid_row && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      const size_t orow = ((size_t)b * n_q + (q0 + pos)) * h_q + hh;
+      uint16_t* op = out + orow * D;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = dt * 32 + 8 * rg + 4 * half;
-        u32x2 w{pack_bf16x2(O[dt][4 * rg] * inv, O[dt][4 * rg + 1] * inv),
-                pack_bf16x2(O[dt][4 * rg + 2] * inv, O[dt][4 * rg + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d0) = w;
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = dt * 32 + 8 * rg + 4 * half;
+          u32x2 w{pack_bf16x2(O[dt][4 * rg] * inv, O[dt][4 * rg + 1] * inv),
+                  pack_bf16x2(O[dt][4 * rg + 2] * inv, O[dt][4 * rg + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + d0) = w;
+        }
       }
+      if (lse && half == 0)
+        lse[orow] = (valid_row && l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
     }
-    if (lse && half == 0)
-      lse[((size_t)b * n_q + (p - p_off)) * h_q + hh] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
-  }
   };
   // visibility of chunk u is computed at the end of iteration u-1, where its LDS reads
   // complete during the barrier wait
@@ -462,9 +467,9 @@ bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len, 
 
 template <int D, int G>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const int32_t* sel,
-                                   void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
-                                   int h_kv, int block, int top_k, float sm_scale,
-                                   hipStream_t stream) {
+                                   void* out, float* lse, int batch, int n_q, int kv_len,
+                                   const int32_t* kv_lens, int kv_stride, int h_q, int h_kv,
+                                   int block, int top_k, float sm_scale, hipStream_t stream) {
   constexpr int MQ = NW * (32 / G);
   const int ntiles = (n_q + MQ - 1) / MQ;
   const long long total = (long long)ntiles * h_kv * batch;
@@ -472,18 +477,20 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
   hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3((unsigned)total), dim3(NW * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse, n_q,
-                     kv_len, h_q, h_kv, block, top_k, sm_scale * kLog2e, ntiles, (int)total);
+                     kv_len, h_q, h_kv, block, top_k, sm_scale * kLog2e, ntiles, (int)total,
+                     kv_lens, kv_stride);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_prefill_d(int group, const void* q, const void* k, const void* v,
                                    const int32_t* sel, void* out, float* lse, int batch, int n_q,
-                                   int kv_len, int h_q, int h_kv, int block, int top_k,
-                                   float sm_scale, hipStream_t stream) {
+                                   int kv_len, const int32_t* kv_lens, int kv_stride, int h_q,
+                                   int h_kv, int block, int top_k, float sm_scale,
+                                   hipStream_t stream) {
 #define QSA_G(g)                                                                             \
-  return launch_prefill_t<D, g>(q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv, block, \
-                                top_k, sm_scale, stream)
+  return launch_prefill_t<D, g>(q, k, v, sel, out, lse, batch, n_q, kv_len, kv_lens, kv_stride, \
+                                h_q, h_kv, block, top_k, sm_scale, stream)
   switch (group) {
     case 1: QSA_G(1);
     case 2: QSA_G(2);
@@ -497,20 +504,20 @@ static hipError_t launch_prefill_d(int group, const void* q, const void* k, cons
 }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, const int32_t* sel,
-                               void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
-                               int h_kv, int d, int block, int top_k, float sm_scale,
-                               hipStream_t stream) {
+                               void* out, float* lse, int batch, int n_q, int kv_len,
+                               const int32_t* kv_lens, int kv_stride, int h_q, int h_kv, int d,
+                               int block, int top_k, float sm_scale, hipStream_t stream) {
   if (batch == 0 || n_q == 0) return hipSuccess;
   const int group = h_q / h_kv;
   if (d == 256)
-    return launch_prefill_bf16_rt(q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv, d, block,
-                                  top_k, sm_scale, stream);
+    return launch_prefill_bf16_rt(q, k, v, sel, out, lse, batch, n_q, kv_len, kv_lens, kv_stride,
+                                  h_q, h_kv, d, block, top_k, sm_scale, stream);
   if (d == 128)
-    return launch_prefill_d<128>(group, q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv,
-                                 block, top_k, sm_scale, stream);
+    return launch_prefill_d<128>(group, q, k, v, sel, out, lse, batch, n_q, kv_len, kv_lens,
+                                 kv_stride, h_q, h_kv, block, top_k, sm_scale, stream);
   if (d == 64)
-    return launch_prefill_d<64>(group, q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv,
-                                block, top_k, sm_scale, stream);
+    return launch_prefill_d<64>(group, q, k, v, sel, out, lse, batch, n_q, kv_len, kv_lens,
+                                kv_stride, h_q, h_kv, block, top_k, sm_scale, stream);
   return hipErrorInvalidValue;
 }
 

@@ -53,8 +53,9 @@ template <int D, int G>
 __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int n_q, int kv_len, int h_q, int h_kv, int block, int top_k,
-    float scale_log2, int ntiles, int total_wg) {
+    float* __restrict__ lse, int n_q, int kv_len_all, int h_q, int h_kv, int block, int top_k,
+    float scale_log2, int ntiles, int total_wg, const int32_t* __restrict__ kv_lens,
+    int kv_stride) {
   constexpr int NW = RT_NW, NS = RT_NS, KC = RT_KC;
   constexpr int NT = NW * 64;
   constexpr int RT = RtTiles<G>::value;
@@ -90,11 +91,14 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
   const int tile = ntiles - 1 - logical % ntiles;
   const int g = (logical / ntiles) % h_kv;
   const int b = logical / (ntiles * h_kv);
+  // keys of this sequence (kv_lens[b] clamped to the K/V slab's kv_stride rows, or the
+  // common length); query rows with p < 0 are padding
+  const int kv_len = kv_lens ? min(max(kv_lens[b], 0), kv_stride) : kv_len_all;
   const int p_off = kv_len - n_q;
   const int q0 = tile * MQ;
   const int p0 = p_off + q0;
   const int p_hi = p_off + min(q0 + MQ, n_q) - 1;
-  const int words = (p_hi / block) / 32 + 1;
+  const int words = p_hi >= 0 ? (p_hi / block) / 32 + 1 : 0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,13 +109,13 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
     const int pos = e / top_k;
     const int p = p0 + pos;
     uint16_t j = kRtNoSel;
-    if (p < kv_len) {
+    if (p >= 0 && p < kv_len) {
       const int jj = sel[((size_t)b * n_q + q0 + pos) * top_k + (e - pos * top_k)];
       if (jj >= 0 && jj < (p + 1) / block) j = (uint16_t)jj;
     }
     sel_s[e] = j;
   }
-  for (int w = tid; w < words; w += NT) bm[w] = 0u;
+  for (int w = tid; w < max(words, 1); w += NT) bm[w] = 0u;
   __syncthreads();
   for (int e = tid; e < MQ * top_k; e += NT) {
     const int j = sel_s[e];
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
   }
   if (tid < MQ) {
     const int p = p0 + tid;
-    if (p < kv_len && (p + 1) % block != 0) {
+    if (p >= 0 && p < kv_len && (p + 1) % block != 0) {
       const int j = p / block;
       atomicOr(&bm[j >> 5], 1u << (j & 31));
     }
@@ -135,12 +139,15 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
     return wave * PW + (16 * rt + col) / G;
   };
   auto p_of = [&](int rt) __attribute__((always_inline)) { return p0 + pos_of(rt); };
+  auto valid_of = [&](int rt) __attribute__((always_inline)) {
+    return p_of(rt) >= 0 && p_of(rt) < kv_len;
+  };
 
   bf16x8 qreg[RT][NKT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int hh = g * G + (16 * rt + col) % G;
-    const int qi = p_of(rt) < kv_len ? p_of(rt) - p_off : 0;
+    const int qi = valid_of(rt) ? p_of(rt) - p_off : 0;
     const uint16_t* qp = q + (((size_t)b * n_q + qi) * h_q + hh) * D + quad * 8;
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
@@ -162,8 +169,8 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
 
   const int nsub = (block + KC - 1) / KC;
   const uint32_t kv_row = (uint32_t)h_kv * D;  // elements between consecutive tokens
-  const uint16_t* kbase = k + ((size_t)b * kv_len * h_kv + g) * D;
-  const uint16_t* vbase = v + ((size_t)b * kv_len * h_kv + g) * D;
+  const uint16_t* kbase = k + ((size_t)b * kv_stride * h_kv + g) * D;
+  const uint16_t* vbase = v + ((size_t)b * kv_stride * h_kv + g) * D;
 
   int nblk = 0;
   for (int w = 0; w < words; ++w) nblk += __builtin_popcount((uint32_t)wave_uniform((int)bm[w]));
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     ptr[rt] = 0;
-    cur_sel[rt] = p_of(rt) < kv_len ? sel_s[pos_of(rt) * top_k] : kRtNoSel;
+    cur_sel[rt] = valid_of(rt) ? sel_s[pos_of(rt) * top_k] : kRtNoSel;
     vis[rt] = false;
   }
   auto visit = [&](bool first) __attribute__((always_inline)) {
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
         }
         // own block: p inside it and not its last token (a non-empty trailing part)
         const int p = p_of(rt);
-        vis[rt] = hit || (p < kv_len && p >= key0 && p <= key0 + block - 2);
+        vis[rt] = hit || (p >= 0 && p < kv_len && p >= key0 && p <= key0 + block - 2);
       }
     }
   };
@@ -400,10 +407,12 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
     for (int rt = 0; rt < RT; ++rt) {
       const float l_tot = quad_sum(l_run[rt]);
       const int p = p_of(rt);
-      if (p < kv_len) {
+      const bool valid = p >= 0 && p < kv_len;
+      // rows past n_q do not exist; padding rows (p < 0) get zeros and lse = -inf
+      if (valid || (p < 0 && p - p_off < n_q)) {
         const int hh = g * G + (16 * rt + col) % G;
         const size_t orow = ((size_t)b * n_q + (p - p_off)) * h_q + hh;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float inv = (valid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
         uint16_t* op = out + orow * D + 4 * quad;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -412,7 +421,8 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
               u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
         }
         if (lse && quad == 0)
-          lse[orow] = l_tot > 0.f ? (m_run[rt] + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+          lse[orow] = (valid && l_tot > 0.f) ? (m_run[rt] + __log2f(l_tot)) * kLn2
+                                             : -__builtin_inff();
       }
     }
   };
@@ -477,8 +487,9 @@ bool prefill_bf16_rt_supported(int group, int d, int block, int top_k, int kv_le
 template <int D, int G>
 static hipError_t launch_prefill_rt_t(const void* q, const void* k, const void* v,
                                       const int32_t* sel, void* out, float* lse, int batch,
-                                      int n_q, int kv_len, int h_q, int h_kv, int block,
-                                      int top_k, float sm_scale, hipStream_t stream) {
+                                      int n_q, int kv_len, const int32_t* kv_lens, int kv_stride,
+                                      int h_q, int h_kv, int block, int top_k, float sm_scale,
+                                      hipStream_t stream) {
   constexpr int MQ = RT_NW * (16 * RtTiles<G>::value / G);
   const int ntiles = (n_q + MQ - 1) / MQ;
   const long long total = (long long)ntiles * h_kv * batch;
@@ -486,19 +497,20 @@ static hipError_t launch_prefill_rt_t(const void* q, const void* k, const void* 
   hipLaunchKernelGGL((prefill_bf16_rt_kernel<D, G>), dim3((unsigned)total), dim3(RT_NW * 64), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse, n_q,
-                     kv_len, h_q, h_kv, block, top_k, sm_scale * kLog2e, ntiles, (int)total);
+                     kv_len, h_q, h_kv, block, top_k, sm_scale * kLog2e, ntiles, (int)total,
+                     kv_lens, kv_stride);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_bf16_rt(const void* q, const void* k, const void* v, const int32_t* sel,
-                                  void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
-                                  int h_kv, int d, int block, int top_k, float sm_scale,
-                                  hipStream_t stream) {
+                                  void* out, float* lse, int batch, int n_q, int kv_len,
+                                  const int32_t* kv_lens, int kv_stride, int h_q, int h_kv, int d,
+                                  int block, int top_k, float sm_scale, hipStream_t stream) {
   if (batch == 0 || n_q == 0) return hipSuccess;
   if (d != 256) return hipErrorInvalidValue;
 #define QSA_G(gg)                                                                          \
-  return launch_prefill_rt_t<256, gg>(q, k, v, sel, out, lse, batch, n_q, kv_len, h_q, h_kv, \
-                                      block, top_k, sm_scale, stream)
+  return launch_prefill_rt_t<256, gg>(q, k, v, sel, out, lse, batch, n_q, kv_len, kv_lens,    \
+                                      kv_stride, h_q, h_kv, block, top_k, sm_scale, stream)
   switch (h_q / h_kv) {
     case 1: QSA_G(1);
     case 2: QSA_G(2);

@@ -141,10 +141,14 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
                   "qsa_index_topk_decode");
 }
 
+// The three prefill calls: the whole sequence (n_q == kv_len), a chunk of the last n_q
+// tokens over a common kv_len, and a batch of sequences of their own lengths kv_lens[b]
+// (K/V slabs of kv_stride rows).
 static qsa_status prefill_impl(const char* fn, const void* q, const void* k, const void* v,
-                               const int32_t* sel, void* out, float* lse, int batch, int n_q,
-                               int kv_len, int h_q, int h_kv, int d, int block, int top_k,
-                               float sm_scale, qsa_dtype dt, hipStream_t stream) {
+                               const int32_t* kv_lens, const int32_t* sel, void* out, float* lse,
+                               int batch, int n_q, int kv_len, int kv_stride, int h_q, int h_kv,
+                               int d, int block, int top_k, float sm_scale, qsa_dtype dt,
+                               hipStream_t stream) {
   QSA_REQUIRE(dtype_ok(dt), QSA_ERR_INVALID_ARGUMENT, "dt must be QSA_F32 or QSA_BF16");
   QSA_REQUIRE(batch >= 0 && n_q >= 0 && kv_len >= 0, QSA_ERR_INVALID_ARGUMENT,
               "batch, n_q and kv_len must be >= 0");
@@ -168,17 +172,18 @@ static qsa_status prefill_impl(const char* fn, const void* q, const void* k, con
   QSA_PTR(out, "out");
   QSA_OPT_PTR(lse, "lse");
   if (dt == QSA_BF16) {
-    QSA_REQUIRE(qsa::prefill_bf16_supported(h_q / h_kv, d, block, top_k, kv_len, h_kv),
+    QSA_REQUIRE(qsa::prefill_bf16_supported(h_q / h_kv, d, block, top_k, kv_stride, h_kv),
                 QSA_ERR_UNSUPPORTED,
                 "bf16 prefill not built for group %d, d %d, block %d, top_k %d, kv_len %d, "
-                "h_kv %d", h_q / h_kv, d, block, top_k, kv_len, h_kv);
-    return from_hip(qsa::launch_prefill_bf16(q, k, v, sel, out, lse, batch, n_q, kv_len, h_q,
-                                             h_kv, d, block, top_k, sm_scale, stream),
+                "h_kv %d", h_q / h_kv, d, block, top_k, kv_stride, h_kv);
+    return from_hip(qsa::launch_prefill_bf16(q, k, v, sel, out, lse, batch, n_q, kv_len, kv_lens,
+                                             kv_stride, h_q, h_kv, d, block, top_k, sm_scale,
+                                             stream),
                     fn);
   }
   return from_hip(qsa::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                       static_cast<const float*>(v), sel, nullptr,
-                                       static_cast<float*>(out), lse, batch, n_q, kv_len, kv_len,
+                                       static_cast<const float*>(v), sel, kv_lens,
+                                       static_cast<float*>(out), lse, batch, n_q, kv_stride, kv_len,
                                        h_q, h_kv, d, block, top_k, sm_scale, stream),
                   fn);
 }
@@ -187,8 +192,8 @@ qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                    const int32_t* sel, void* out, float* lse, int batch, int seq,
                                    int h_q, int h_kv, int d, int block, int top_k,
                                    float sm_scale, qsa_dtype dt, hipStream_t stream) {
-  return prefill_impl("qsa_sparse_attn_prefill", q, k, v, sel, out, lse, batch, seq, seq, h_q,
-                      h_kv, d, block, top_k, sm_scale, dt, stream);
+  return prefill_impl("qsa_sparse_attn_prefill", q, k, v, nullptr, sel, out, lse, batch, seq, seq,
+                      seq, h_q, h_kv, d, block, top_k, sm_scale, dt, stream);
 }
 
 qsa_status qsa_sparse_attn_prefill_chunk(const void* q, const void* k, const void* v,
@@ -196,8 +201,19 @@ qsa_status qsa_sparse_attn_prefill_chunk(const void* q, const void* k, const voi
                                          int n_q, int kv_len, int h_q, int h_kv, int d, int block,
                                          int top_k, float sm_scale, qsa_dtype dt,
                                          hipStream_t stream) {
-  return prefill_impl("qsa_sparse_attn_prefill_chunk", q, k, v, sel, out, lse, batch, n_q,
-                      kv_len, h_q, h_kv, d, block, top_k, sm_scale, dt, stream);
+  return prefill_impl("qsa_sparse_attn_prefill_chunk", q, k, v, nullptr, sel, out, lse, batch,
+                      n_q, kv_len, kv_len, h_q, h_kv, d, block, top_k, sm_scale, dt, stream);
+}
+
+qsa_status qsa_sparse_attn_prefill_varlen(const void* q, const void* k, const void* v,
+                                          const int32_t* kv_lens, const int32_t* sel, void* out,
+                                          float* lse, int batch, int n_q, int max_len, int h_q,
+                                          int h_kv, int d, int block, int top_k, float sm_scale,
+                                          qsa_dtype dt, hipStream_t stream) {
+  QSA_REQUIRE(batch == 0 || n_q == 0 || kv_lens != nullptr, QSA_ERR_INVALID_ARGUMENT,
+              "kv_lens must not be NULL");
+  return prefill_impl("qsa_sparse_attn_prefill_varlen", q, k, v, kv_lens, sel, out, lse, batch,
+                      n_q, max_len, max_len, h_q, h_kv, d, block, top_k, sm_scale, dt, stream);
 }
 
 qsa_status qsa_sparse_attn_decode_workspace_size(int batch, int h_q, int h_kv, int d, int block,

@@ -34,18 +34,20 @@ hipError_t launch_index_topk_decode(const void* iq, const void* ik, float* cmp,
 constexpr int kPrefillSelCap = 8192;
 constexpr int kPrefillMaxBlocks = 4096;
 bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len, int h_kv);
-// n_q query rows at positions kv_len - n_q .. kv_len - 1 over kv_len keys.
+// n_q query rows at positions kv_len - n_q .. kv_len - 1 over kv_len keys, where kv_len is
+// kv_lens[b] clamped to [0, kv_stride] when kv_lens is given (else the common kv_len); K/V
+// hold kv_stride rows per sequence; rows with a negative position are padding (zeros).
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, const int32_t* sel,
-                               void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
-                               int h_kv, int d, int block, int top_k, float sm_scale,
-                               hipStream_t stream);
+                               void* out, float* lse, int batch, int n_q, int kv_len,
+                               const int32_t* kv_lens, int kv_stride, int h_q, int h_kv, int d,
+                               int block, int top_k, float sm_scale, hipStream_t stream);
 // The head-dim-256 instance (16-row tiles, 32-key chunks); launch_prefill_bf16 and
 // prefill_bf16_supported route d = 256 here.
 bool prefill_bf16_rt_supported(int group, int d, int block, int top_k, int kv_len, int h_kv);
 hipError_t launch_prefill_bf16_rt(const void* q, const void* k, const void* v, const int32_t* sel,
-                                  void* out, float* lse, int batch, int n_q, int kv_len, int h_q,
-                                  int h_kv, int d, int block, int top_k, float sm_scale,
-                                  hipStream_t stream);
+                                  void* out, float* lse, int batch, int n_q, int kv_len,
+                                  const int32_t* kv_lens, int kv_stride, int h_q, int h_kv, int d,
+                                  int block, int top_k, float sm_scale, hipStream_t stream);
 
 // float32 attention (prefill and decode) on the vector ALUs.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const int32_t* sel,

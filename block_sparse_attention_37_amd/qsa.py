@@ -38,6 +38,8 @@ SIGNATURES = {
     "qsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "qsa_sparse_attn_prefill_chunk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                            _I, _P]),
+    "qsa_sparse_attn_prefill_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                            _I, _F, _I, _P]),
     "qsa_sparse_attn_decode_workspace_size": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)]),
     "qsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                     _P, _Z, _I, _P]),
@@ -238,6 +240,36 @@ def sparse_attn_prefill_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return (out, lse) if lse is not None else out
 
 
+def sparse_attn_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               kv_lens: torch.Tensor, sel: torch.Tensor, block: int,
+                               sm_scale: float | None = None, return_lse: bool = False,
+                               out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Prefill of a batch of sequences of their own lengths kv_lens[b]: q [batch, n_q, h_q, d]
+    holds each sequence's last n_q tokens right-aligned (query i at position
+    kv_lens[b] - n_q + i; rows with a negative position are padding and come out 0),
+    k, v [batch, max_len, h_kv, d] hold each sequence from row 0."""
+    batch, n_q, h_q, d = q.shape
+    max_len, h_kv = k.shape[1], k.shape[2]
+    _expect(k, (batch, max_len, h_kv, d), q.dtype, "k")
+    _expect(v, (batch, max_len, h_kv, d), q.dtype, "v")
+    _expect(kv_lens, (batch,), torch.int32, "kv_lens")
+    top_k = sel.shape[2]
+    _expect(sel, (batch, n_q, top_k), torch.int32, "sel")
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    if return_lse and lse is None:
+        lse = torch.empty(batch, n_q, h_q, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, (batch, n_q, h_q), torch.float32, "lse")
+    dev = _dev(q, k, v, kv_lens, sel, out, lse)
+    _call("qsa_sparse_attn_prefill_varlen", _ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), _ptr(sel),
+          _ptr(out), _ptr(lse), batch, n_q, max_len, h_q, h_kv, d, block, top_k, scale, _dt(q),
+          _stream(dev))
+    return (out, lse) if lse is not None else out
+
+
 def decode_workspace_bytes(batch: int, h_q: int, h_kv: int, d: int, block: int, top_k: int) -> int:
     n = ctypes.c_size_t(0)
     _call("qsa_sparse_attn_decode_workspace_size", batch, h_q, h_kv, d, block, top_k, ctypes.byref(n))
@@ -359,6 +391,49 @@ class PrefillPlan:
 
     def run_attention(self):
         _call(self._attn_fn, *self._attn, _stream(self.dev))
+
+    def run(self):
+        self.run_index()
+        self.run_attention()
+        return self.out
+
+
+class VarlenPrefillPlan:
+    """compress -> index/top-k -> sparse attention for a batch of sequences of their own
+    lengths ``kv_lens`` [batch] (device int32): q, iq [batch, n_q, ...] right-aligned (the
+    last n_q tokens of each sequence, padding rows in front of the shorter ones), k, v, ik
+    [batch, max_len, ...] from row 0."""
+
+    def __init__(self, q, k, v, iq, ik, kv_lens, block: int, top_k: int,
+                 sm_scale: float | None = None):
+        batch, n_q, h_q, d = q.shape
+        max_len, h_kv = k.shape[1], k.shape[2]
+        h_idx, d_idx = iq.shape[-2:]
+        _expect(kv_lens, (batch,), torch.int32, "kv_lens")
+        dev = _dev(q, k, v, iq, ik, kv_lens)
+        self.block, self.top_k, self.dev = block, top_k, dev
+        self.cmp = torch.zeros(batch, max_len // block, d_idx, dtype=torch.float32, device=dev)
+        self.sel = torch.empty(batch, n_q, top_k, dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty(batch, n_q, h_q, dtype=torch.float32, device=dev)
+        self.kv_lens = kv_lens
+        scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+        self._keep = (q, k, v, iq, ik, kv_lens)
+        self._compress = (_ptr(ik), _ptr(kv_lens), _ptr(self.cmp), batch, max_len, d_idx, block,
+                          _dt(ik))
+        self._index = (_ptr(iq), _ptr(self.cmp), _ptr(kv_lens), _ptr(self.sel), None, batch,
+                       n_q, h_idx, d_idx, max_len // block, block, top_k, _dt(iq))
+        self._attn = (_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), _ptr(self.sel), _ptr(self.out),
+                      _ptr(self.lse), batch, n_q, max_len, h_q, h_kv, d, block, top_k, scale,
+                      _dt(q))
+
+    def run_index(self):
+        s = _stream(self.dev)
+        _call("qsa_compress_keys", *self._compress, s)
+        _call("qsa_index_topk", *self._index, s)
+
+    def run_attention(self):
+        _call("qsa_sparse_attn_prefill_varlen", *self._attn, _stream(self.dev))
 
     def run(self):
         self.run_index()

@@ -31,7 +31,7 @@ T_Q, T_K, T_V, T_IQ, T_IK, T_MU, T_PLANT, T_LENS = range(8)
 class Workload:
     name: str
     seed: int
-    kind: str                 # "prefill" | "decode"
+    kind: str                 # "prefill" | "decode" | "varlen" (prefill of mixed lengths)
     dtype: str                # "bf16" | "f32"
     batch: int
     block: int
@@ -42,8 +42,8 @@ class Workload:
     h_idx: int
     d_idx: int
     seq: int = 0              # prefill prompt length
-    max_len: int = 0          # decode cache rows
-    len_lo: int = 0           # decode context lengths, inclusive range
+    max_len: int = 0          # decode cache rows (varlen: K/V rows per sequence)
+    len_lo: int = 0           # decode context (varlen: prompt) lengths, inclusive range
     len_hi: int = 0
     query_mean: bool = False
     plant_frac: float = 0.0   # fraction of complete blocks planted (seeded choice)
@@ -90,6 +90,12 @@ WORKLOADS = {
         "prefill_bf16_d256_32k", 6, "prefill", "bf16", batch=1, seq=32768 + 45, block=128,
         top_k=32, h_q=16, h_kv=2, d=256, h_idx=8, d_idx=64, query_mean=True, plant_every=16,
         note="head dim 256, 16/2 heads; 256 complete blocks + 45 trailing"),
+    # a batch of prompts of mixed length, left-padded to the longest (varlen prefill)
+    "varlen_prefill_bf16_b8": Workload(
+        "varlen_prefill_bf16_b8", 8, "varlen", "bf16", batch=8, max_len=16384, len_lo=1024,
+        len_hi=16384, block=64, top_k=16, h_q=16, h_kv=2, d=128, h_idx=8, d_idx=64,
+        query_mean=True, plant_frac=0.05,
+        note="8 prompts, lengths uniform in [1024, 16384]; queries right-aligned to the longest"),
     "decode_bf16_d256_b64": Workload(
         "decode_bf16_d256_b64", 7, "decode", "bf16", batch=64, max_len=32768, len_lo=8192,
         len_hi=32768, block=64, top_k=32, h_q=16, h_kv=2, d=256, h_idx=8, d_idx=64,
@@ -174,6 +180,15 @@ def prefill_inputs(w: Workload, seq_id: int = 0) -> dict:
     iq = _indexer_queries(w, seq_id, T)
     ik = _indexer_keys(w, seq_id, T, iq)
     return dict(q=q, k=k, v=v, iq=iq, ik=ik)
+
+
+def varlen_inputs(w: Workload, seqs=None):
+    """Prompts of a varlen batch: (lens, {b: prefill_inputs of length lens[b]}) for b in
+    ``seqs`` (default all); lengths are drawn as for decode (tensor id 7)."""
+    lens = decode_lens(w)
+    seqs = range(w.batch) if seqs is None else seqs
+    return lens, {b: prefill_inputs(w.with_(seq=int(lens[b]), kind="prefill"), seq_id=b)
+                  for b in seqs}
 
 
 def decode_lens(w: Workload) -> np.ndarray:

@@ -102,7 +102,8 @@ qsa_status qsa_compress_keys(const void* ik, const int32_t* kv_lens, float* cmp,
  *
  *   iq          [batch, n_q, h_idx, d_idx]   element type dt
  *   cmp         [batch, max_blocks, d_idx]   float32 (from qsa_compress_keys)
- *   kv_lens     [batch] int32 or NULL; values in [n_q, max_blocks*block + block - 1]
+ *   kv_lens     [batch] int32 or NULL; values <= max_blocks*block + block - 1; a value
+ *               below n_q makes the rows with p < 0 padding (every slot -1)
  *   sel         [batch, n_q, top_k] int32 output: the kept block ids in ascending order,
  *               then -1 in the remaining top_k - m slots
  *   sel_scores  [batch, n_q, top_k] float32 output or NULL: S of each kept block in the
@@ -196,6 +197,30 @@ qsa_status qsa_sparse_attn_prefill_chunk(const void* q, const void* k, const voi
                                          int batch, int n_q, int kv_len, int h_q, int h_kv,
                                          int d, int block, int top_k, float sm_scale,
                                          qsa_dtype dt, hipStream_t stream);
+
+/*
+ * Steps 4 + 5 for a batch of sequences of different lengths (Qwen4-Exp, as above; batched
+ * generation pads the shorter prompts on the left, and every query still attends only to
+ * its own sequence's tokens).  Sequence b has len_b = kv_lens[b] tokens (clamped to
+ * [0, max_len]); its queries are the last n_q rows of q[b], right-aligned: query row i sits
+ * at p = len_b - n_q + i, the rule qsa_index_topk applies with the same kv_lens and n_q.
+ * Rows with p < 0 are padding: out is 0 there and lse is -inf.  With n_q = max_b len_b and
+ * kv_lens the prompt lengths this is a batched prefill of prompts of mixed length; with
+ * n_q <= min_b len_b it is a chunk appended to caches of mixed length.
+ *
+ *   q, out   [batch, n_q, h_q, d]         element type dt (out may not alias any input)
+ *   k, v     [batch, max_len, h_kv, d]    element type dt; rows >= len_b are not read
+ *   kv_lens  [batch] int32 (device)
+ *   sel      [batch, n_q, top_k] int32, as for qsa_sparse_attn_prefill (padding rows: -1)
+ *   lse      [batch, n_q, h_q] float32 output or NULL
+ * Invalid: kv_lens NULL (when batch and n_q are non-zero); n_q > max_len.
+ * Supported: as qsa_sparse_attn_prefill with seq = max_len.
+ */
+qsa_status qsa_sparse_attn_prefill_varlen(const void* q, const void* k, const void* v,
+                                          const int32_t* kv_lens, const int32_t* sel, void* out,
+                                          float* lse, int batch, int n_q, int max_len, int h_q,
+                                          int h_kv, int d, int block, int top_k, float sm_scale,
+                                          qsa_dtype dt, hipStream_t stream);
 
 /*
  * Bytes of device workspace qsa_sparse_attn_decode needs for these sizes (may be 0).

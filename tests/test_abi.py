@@ -125,6 +125,12 @@ def test_prefill_validation(qsa_lib):
     assert "kv_len" in _err()
     assert chunk(-1, 100) == INVALID
     assert chunk(0, 100) == 0
+    varlen = lambda kvl, n_q, max_len: L.qsa_sparse_attn_prefill_varlen(
+        FAKE, FAKE, FAKE, kvl, FAKE, FAKE, None, 2, n_q, max_len, 8, 2, 128, 16, 4, 0.1, 1, None)
+    assert varlen(None, 10, 100) == INVALID
+    assert "kv_lens" in _err()
+    assert varlen(FAKE, 200, 100) == INVALID
+    assert varlen(None, 0, 100) == 0
 
 
 def test_decode_validation(qsa_lib):

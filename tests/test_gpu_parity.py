@@ -153,6 +153,73 @@ def test_prefill_chunk(gpu, case):
     assert e_lse <= LSE_ATOL[w.dtype], f"lse max-abs error {e_lse}"
 
 
+VARLEN_PREFILL = [
+    # (workload for the shapes, prompt lengths, n_q): query rows right-aligned, K/V from row 0
+    (_wl("varlen_g8_d128", seq=0, block=32, top_k=3, h_q=8, h_kv=2, d=128, h_idx=3, d_idx=64,
+         query_mean=True, plant_frac=0.2), [1, 100, 257, 300], 300),
+    (_wl("varlen_g4_d64_empty_seq", seq=0, block=16, top_k=4, h_q=8, h_kv=2, d=64),
+     [0, 5, 64, 200], 200),
+    (_wl("varlen_chunks_mixed_caches", seq=0, block=16, top_k=5, h_q=2, h_kv=2, d=128),
+     [300, 257, 400], 50),
+    (_wl("varlen_g32_d64", seq=0, block=16, top_k=2, h_q=32, h_kv=1, d=64), [20, 70], 70),
+    (_wl("varlen_d256", seq=0, block=32, top_k=2, h_q=16, h_kv=2, d=256), [70, 130], 130),
+    (_wl("varlen_f32", seq=0, block=8, top_k=3, h_q=4, h_kv=2, d=64, dtype="f32"), [10, 77],
+     77),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_PREFILL, ids=lambda c: c[0].name)
+def test_prefill_varlen(gpu, case):
+    """A batch of prompts of their own lengths through compress (kv_lens), index (kv_lens,
+    n_q) and qsa_sparse_attn_prefill_varlen: every valid row against the oracle run on
+    that prompt alone; padding rows (position < 0) give sel -1, out 0 and lse -inf."""
+    w, lens, n_q = case
+    say(f"case varlen {w.name} lens={lens} n_q={n_q}")
+    B, nb = w.block, len(lens)
+    max_len = max(max(lens), n_q) + 3  # rows past every prompt are never read
+    seqs = [S.prefill_inputs(w.with_(seq=L), seq_id=b) for b, L in enumerate(lens)]
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q = torch.zeros(nb, n_q, w.h_q, w.d, dtype=dt, device=gpu)
+    iq = torch.zeros(nb, n_q, w.h_idx, w.d_idx, dtype=dt, device=gpu)
+    k = torch.full((nb, max_len, w.h_kv, w.d), 7.0, dtype=dt, device=gpu)
+    v = torch.full_like(k, -7.0)
+    ik = torch.full((nb, max_len, w.d_idx), 5.0, dtype=dt, device=gpu)
+    for b, (L, x) in enumerate(zip(lens, seqs)):
+        r = min(L, n_q)
+        if r:
+            q[b, n_q - r:] = _t(x["q"][L - r:], gpu)
+            iq[b, n_q - r:] = _t(x["iq"][L - r:], gpu)
+        if L:
+            k[b, :L], v[b, :L], ik[b, :L] = _t(x["k"], gpu), _t(x["v"], gpu), _t(x["ik"], gpu)
+    kvl = torch.tensor(lens, dtype=torch.int32, device=gpu)
+    cmp = Q.compress_keys(ik, B, kv_lens=kvl)
+    sel = Q.index_topk(iq, cmp, B, w.top_k, kv_lens=kvl)
+    out, lse = Q.sparse_attn_prefill_varlen(q, k, v, kvl, sel, B, w.sm_scale, return_lse=True)
+    torch.cuda.synchronize()
+    sel_n, out_n, lse_n = sel.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy()
+    worst = 0.0
+    for b, (L, x) in enumerate(zip(lens, seqs)):
+        r = min(L, n_q)
+        pad = n_q - r
+        assert np.all(sel_n[b, :pad] == -1), f"seq {b}: padding rows selected blocks"
+        assert np.all(out_n[b, :pad] == 0.0), f"seq {b}: padding rows not zero"
+        assert np.all(np.isneginf(lse_n[b, :pad])), f"seq {b}: padding lse not -inf"
+        if r == 0:
+            continue
+        q64, k64, v64 = S.to_f64(x["q"]), S.to_f64(x["k"]), S.to_f64(x["v"])
+        cmp_o = O.compress_keys(S.to_f64(x["ik"]), B)
+        fails, _ = check_selection(sel_n[b, pad:], S.to_f64(x["iq"])[L - r:], cmp_o, L, B,
+                                   w.top_k)
+        assert not fails, f"seq {b}: " + "\n".join(fails[:5])
+        out_o, lse_o = O.attend_rows(q64[L - r:], k64, v64, sel_n[b, pad:],
+                                     np.arange(L - r, L), range(r), B, w.sm_scale)
+        e_out, e_lse = max_abs(out_n[b, pad:], out_o), max_abs(lse_n[b, pad:], lse_o)
+        worst = max(worst, e_out)
+        assert e_out <= OUT_ATOL[w.dtype], f"seq {b}: out max-abs error {e_out}"
+        assert e_lse <= LSE_ATOL[w.dtype], f"seq {b}: lse max-abs error {e_lse}"
+    say(f"  worst out err={worst:.3g}")
+
+
 def test_prefill_batch2(gpu):
     w = _wl("batch2", seq=150, block=16, top_k=3, h_q=8, h_kv=2, d=128, batch=2)
     say("case prefill batch2")
@@ -253,6 +320,45 @@ def test_prefill_bf16_d256_32k_sampled(gpu):
     sel_rows = _stratified_rows(w.seq, w.block, 3000, 9)
     att_rows = _stratified_rows(w.seq, w.block, 150, 10)[:300]
     check_prefill(w, inp, res, rows=att_rows, sel_rows=sel_rows)
+
+
+def test_varlen_prefill_bf16_b8_sampled(gpu):
+    """The varlen bench workload (8 prompts of 1k..16k tokens, as bench.py lays them out):
+    selection on sampled rows of every prompt and attention on fewer, against the oracle
+    run per prompt."""
+    w = S.WORKLOADS["varlen_prefill_bf16_b8"]
+    say(f"case {w.name}: generating inputs")
+    lens, seqs = S.varlen_inputs(w)
+    n_q, B = int(lens.max()), w.block
+    dt = torch.bfloat16
+    q = torch.zeros(w.batch, n_q, w.h_q, w.d, dtype=dt, device=gpu)
+    iq = torch.zeros(w.batch, n_q, w.h_idx, w.d_idx, dtype=dt, device=gpu)
+    k = torch.zeros(w.batch, w.max_len, w.h_kv, w.d, dtype=dt, device=gpu)
+    v, ik = torch.zeros_like(k), torch.zeros(w.batch, w.max_len, w.d_idx, dtype=dt, device=gpu)
+    for b, x in seqs.items():
+        L = int(lens[b])
+        q[b, n_q - L:], iq[b, n_q - L:] = _t(x["q"], gpu), _t(x["iq"], gpu)
+        k[b, :L], v[b, :L], ik[b, :L] = _t(x["k"], gpu), _t(x["v"], gpu), _t(x["ik"], gpu)
+    kvl = torch.from_numpy(lens.astype(np.int32)).to(gpu)
+    plan = Q.VarlenPrefillPlan(q, k, v, iq, ik, kvl, B, w.top_k, w.sm_scale)
+    plan.run()
+    torch.cuda.synchronize()
+    sel_n, out_n = plan.sel.cpu().numpy(), plan.out.float().cpu().numpy()
+    for b, x in seqs.items():
+        L = int(lens[b])
+        pad = n_q - L
+        assert np.all(out_n[b, :pad] == 0.0) and np.all(sel_n[b, :pad] == -1)
+        cmp_o = O.compress_keys(S.to_f64(x["ik"]), B)
+        rows = _stratified_rows(L, B, 300, 20 + b)
+        fails, _ = check_selection(sel_n[b, pad:], S.to_f64(x["iq"]), cmp_o, L, B, w.top_k,
+                                   rows=rows)
+        assert not fails, f"seq {b}: " + "\n".join(fails[:5])
+        att = rows[:: max(1, len(rows) // 24)]
+        out_o, _ = O.attend_rows(S.to_f64(x["q"]), S.to_f64(x["k"]), S.to_f64(x["v"]),
+                                 sel_n[b, pad:], np.arange(L), att, B, w.sm_scale)
+        e = max_abs(out_n[b, pad:][att], out_o)
+        say(f"  seq {b}: L={L} rows={len(att)} out err={e:.3g}")
+        assert e <= OUT_ATOL["bf16"], f"seq {b}: out error {e}"
 
 
 @pytest.mark.slow
