@@ -18,7 +18,10 @@ A step is one pass of the whole QSA path over one batch of synthetic input:
                      before timing).
 Inputs are resident in HBM before the timed region starts.  ``value`` is
 tokens/s of the whole step (prefill: batch*seq tokens, varlen: the prompts' tokens,
-decode: batch tokens).
+decode: batch tokens).  With ``--graph`` (the default) the steps are launched from a
+HIP graph that holds ``steps_per_graph`` consecutive whole steps (the largest divisor
+of K up to 16), replayed K / steps_per_graph times: every timed step runs all of its
+kernels, in stream order; only the fixed cost of launching a graph is shared.
 
 ``roofline`` describes the dominant kernel (the attention kernel): algorithmic
 flops (prefill, bf16 matrix cores) or algorithmic bytes (decode, HBM) per launch
@@ -112,6 +115,11 @@ def decode_attention_bytes(w, lens) -> float:
     tsz = np.minimum(w.top_k, L // w.block) * w.block + L % w.block
     kv = float(tsz.sum()) * w.h_kv * w.d * esz * 2
     return kv + 2.0 * w.batch * w.h_q * w.d * esz + w.batch * w.top_k * 4 + w.batch * 4
+
+
+def graph_steps(steps: int, most: int = 16) -> int:
+    """Steps captured in one graph: the largest divisor of `steps` up to `most`."""
+    return max(d for d in range(1, min(most, steps) + 1) if steps % d == 0)
 
 
 def kernel_src_hash() -> str:
@@ -296,26 +304,29 @@ def main():
     t_setup = time.perf_counter() - t_setup
 
     stream = torch.cuda.current_stream(dev)
-    if args.graph:
-        # one graph per step: index (+ compression for prefill), then attention
-        g_step = torch.cuda.CUDAGraph()
-        plan.run()  # warm the launch path before capture
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g_step):
-            plan.run()
-        torch.cuda.synchronize()
-        run_step = g_step.replay
-    else:
-        run_step = plan.run
-
     for _ in range(warmup):
-        run_step()
+        plan.run()
     torch.cuda.synchronize()
+    if args.graph:
+        # one graph holds `per_graph` consecutive whole steps (index (+ compression for
+        # prefill), then attention, in stream order); a graph launch costs several
+        # microseconds of its own, so the timed steps replay it steps / per_graph times
+        per_graph = graph_steps(steps)
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            for _ in range(per_graph):
+                plan.run()
+        g_step.replay()  # untimed: instantiates the graph
+        torch.cuda.synchronize()
+        run_step, launches = g_step.replay, steps // per_graph
+    else:
+        per_graph = 0
+        run_step, launches = plan.run, steps
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(steps):
+    for i in range(launches):
         run_step()
     end.record(stream)
     torch.cuda.synchronize()
@@ -368,7 +379,7 @@ def main():
 
     cfg = {"workload": w.name, "kind": w.kind, "batch": w.batch, "block": w.block,
            "top_k": w.top_k, "h_q": w.h_q, "h_kv": w.h_kv, "d": w.d, "h_idx": w.h_idx,
-           "d_idx": w.d_idx, "graph": bool(args.graph)}
+           "d_idx": w.d_idx, "graph": bool(args.graph), "steps_per_graph": per_graph}
     if w.kind == "prefill":
         cfg["seq"] = w.seq
         if w.n_q:
