@@ -28,8 +28,8 @@ flops (prefill, bf16 matrix cores) or algorithmic bytes (decode, HBM) per launch
 divided by its average launch time, measured with events recorded on the stream
 the kernels run on around `steps` back-to-back attention calls that follow the
 timed steps.  ``traffic`` is the HBM byte count per launch from the committed
-profiler counter summary of the workload (null when the kernel sources changed
-since it was taken).
+profiler counter summary of the workload (null when the attention kernel's sources
+changed since it was taken).
 ``cpu_baseline`` times the fp64 oracle (single-threaded BLAS) on a bounded
 sample of the same workload.
 
@@ -122,25 +122,37 @@ def graph_steps(steps: int, most: int = 16) -> int:
     return max(d for d in range(1, min(most, steps) + 1) if steps % d == 0)
 
 
-def kernel_src_hash() -> str:
+# Sources the attention kernel of each workload kind is compiled from (with the build
+# script, whose flags shape the code): the committed counter summaries stay valid while
+# these are unchanged.
+ATTN_SOURCES = {
+    "prefill": ("k_prefill.hip", "k_prefill_rt.hip", "prefill_common.h", "qsa_device.h",
+                "qsa_internal.h"),
+    "decode": ("k_decode.hip", "qsa_device.h", "qsa_internal.h"),
+}
+
+
+def kernel_src_hash(kind: str) -> str:
+    """Hash of the attention kernel's sources for a workload kind (varlen: prefill)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "block_sparse_attention_37_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    pkg = os.path.join(ROOT, "block_sparse_attention_37_amd")
+    files = [os.path.join("csrc", n) for n in ATTN_SOURCES["decode" if kind == "decode" else "prefill"]]
+    for name in files + ["build.py"]:
+        with open(os.path.join(pkg, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, kind: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary of this workload, if it was taken on the current kernel sources."""
+    summary of this workload, if it was taken on the current attention kernel sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_src_sha") != kernel_src_hash():
+    if t.get("kernel_src_sha") != kernel_src_hash(kind):
         return None
     return t.get("bytes_per_launch")
 
@@ -365,7 +377,7 @@ def main():
         achieved = work / (att_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = load_traffic(w.name)
+    roof["traffic"] = load_traffic(w.name, w.kind)
     # the attention call: one kernel for prefill; split kernel + merge kernel for decode
     roof["kernel"] = (("qsa::prefill_bf16_rt_kernel" if w.d == 256 else "qsa::prefill_bf16_kernel")
                       if w.kind in ("prefill", "varlen")
