@@ -107,6 +107,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
 
+  // ---- this lane's query row; its Q loads are issued first, so that their latency
+  // overlaps the selection rows' loads and the bitmap ----
+  const int row = lane & 31;
+  const int half = lane >> 5;
+  const int pos = wave * PW + row / G;
+  const int hh = g * G + row % G;
+  const int p = p0 + pos;
+  const bool valid_row = p >= 0 && p < kv_len;
+  const bool pad_row = p < 0 && q0 + pos < n_q;  // a padding row: zero output
+  const int own_block = (valid_row && (p + 1) % block != 0) ? p / block : -1;
+  u32x4 qraw[NKS];
+  {
+    const uint16_t* qp = q + (((size_t)b * n_q + (valid_row ? p - p_off : 0)) * h_q + hh) * D + half * 8;
+#pragma unroll
+    for (int t = 0; t < NKS; ++t) qraw[t] = *reinterpret_cast<const u32x4*>(qp + t * 16);
+  }
+
   // ---- selection rows of the tile -> LDS; union bitmap ----
   for (int e = tid; e < MQ * top_k; e += NT) {
     const int pos = e / top_k;
@@ -133,27 +150,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   }
   __syncthreads();
 
-  // ---- this lane's query row ----
-  const int row = lane & 31;
-  const int half = lane >> 5;
-  const int pos = wave * PW + row / G;
-  const int hh = g * G + row % G;
-  const int p = p0 + pos;
-  const bool valid_row = p >= 0 && p < kv_len;
-  const bool pad_row = p < 0 && q0 + pos < n_q;  // a padding row: zero output
-  const int own_block = (valid_row && (p + 1) % block != 0) ? p / block : -1;
-
   bf16x8 qreg[NKS];
-  {
-    const uint16_t* qp = q + (((size_t)b * n_q + (valid_row ? p - p_off : 0)) * h_q + hh) * D + half * 8;
 #pragma unroll
-    for (int t = 0; t < NKS; ++t) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qp + t * 16);
-      // opaque to the optimizer: keeps Q in registers instead of re-loading it per chunk
-      // (a re-load would also wait on the untracked K/V loads in flight)
-      keep_in_register(w);
-      qreg[t] = bitcast<bf16x8>(w);
-    }
+  for (int t = 0; t < NKS; ++t) {
+    // opaque to the optimizer: keeps Q in registers instead of re-loading it per chunk
+    // (a re-load would also wait on the untracked K/V loads in flight)
+    keep_in_register(qraw[t]);
+    qreg[t] = bitcast<bf16x8>(qraw[t]);
   }
 
   float m_run = -__builtin_inff();

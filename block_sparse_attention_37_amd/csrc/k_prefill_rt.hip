@@ -104,6 +104,30 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
 
+  // ---- this lane's query rows: column `col` of each row tile; `quad` picks 4 keys of a
+  // 16-key tile (S^T, O^T rows) or 8 elements of an operand.  Their Q loads are issued
+  // first, so that their latency overlaps the selection rows' loads and the bitmap ----
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  // position of row tile rt (16 * rt + col < 32 when G = 32)
+  auto pos_of = [&](int rt) __attribute__((always_inline)) {
+    return wave * PW + (16 * rt + col) / G;
+  };
+  auto p_of = [&](int rt) __attribute__((always_inline)) { return p0 + pos_of(rt); };
+  auto valid_of = [&](int rt) __attribute__((always_inline)) {
+    return p_of(rt) >= 0 && p_of(rt) < kv_len;
+  };
+
+  u32x4 qraw[RT][NKT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int hh = g * G + (16 * rt + col) % G;
+    const int qi = valid_of(rt) ? p_of(rt) - p_off : 0;
+    const uint16_t* qp = q + (((size_t)b * n_q + qi) * h_q + hh) * D + quad * 8;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t) qraw[rt][t] = *reinterpret_cast<const u32x4*>(qp + t * 32);
+  }
+
   // ---- selection rows of the tile -> LDS; union bitmap ----
   for (int e = tid; e < MQ * top_k; e += NT) {
     const int pos = e / top_k;
@@ -130,32 +154,14 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
   }
   __syncthreads();
 
-  // ---- this lane's query rows: column `col` of each row tile; `quad` picks 4 keys of a
-  // 16-key tile (S^T, O^T rows) or 8 elements of an operand ----
-  const int col = lane & 15;
-  const int quad = lane >> 4;
-  // position of row tile rt (16 * rt + col < 32 when G = 32)
-  auto pos_of = [&](int rt) __attribute__((always_inline)) {
-    return wave * PW + (16 * rt + col) / G;
-  };
-  auto p_of = [&](int rt) __attribute__((always_inline)) { return p0 + pos_of(rt); };
-  auto valid_of = [&](int rt) __attribute__((always_inline)) {
-    return p_of(rt) >= 0 && p_of(rt) < kv_len;
-  };
-
   bf16x8 qreg[RT][NKT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int hh = g * G + (16 * rt + col) % G;
-    const int qi = valid_of(rt) ? p_of(rt) - p_off : 0;
-    const uint16_t* qp = q + (((size_t)b * n_q + qi) * h_q + hh) * D + quad * 8;
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(qp + t * 32);
-      keep_in_register(w);  // Q stays in registers (no re-load behind the untracked loads)
-      qreg[rt][t] = bitcast<bf16x8>(w);
+      keep_in_register(qraw[rt][t]);  // Q stays in registers (no re-load behind the untracked loads)
+      qreg[rt][t] = bitcast<bf16x8>(qraw[rt][t]);
     }
-  }
 
   float m_run[RT], l_run[RT];
   f32x4 O[NDT][RT];
