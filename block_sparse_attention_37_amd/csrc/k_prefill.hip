@@ -83,12 +83,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   __shared__ uint16_t sel_s[kPrefillSelCap];       // [MQ][top_k]; block ids < 4096
   __shared__ uint32_t bm[kPrefillMaxBlocks / 32];  // union bitmap
 
-  // ---- which tile: consecutive tiles of one head land on the same XCD (L2); tiles are
-  // dispatched from the end of the sequence (most candidate blocks) backwards, so the last
-  // workgroups to start are the cheap ones near the beginning ----
+  // ---- which tile: runs of consecutive tiles of one head share an XCD (L2), and every
+  // XCD gets a share of every sequence (tile_order); tiles are dispatched from the end of
+  // the sequence (most candidate blocks) backwards, so the last workgroups to start are
+  // the cheap ones near the beginning ----
   const int wg = blockIdx.x;
-  const int per = total_wg / 8;
-  const int logical = (wg < per * 8) ? (wg % 8) * per + wg / 8 : wg;
+  const int logical = tile_order(wg, total_wg);
   const int tile = ntiles - 1 - logical % ntiles;
   const int g = (logical / ntiles) % h_kv;
   const int b = logical / (ntiles * h_kv);

@@ -83,11 +83,10 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
   __shared__ uint16_t sel_s[kPrefillSelCap];       // [MQ][top_k]
   __shared__ uint32_t bm[kPrefillMaxBlocks / 32];  // union bitmap
 
-  // ---- tile order as in the 32-row kernel: consecutive tiles of a head on one XCD,
-  // heaviest (last) tiles first ----
+  // ---- tile order as in the 32-row kernel (tile_order: runs of consecutive tiles per
+  // XCD), heaviest (last) tiles first ----
   const int wg = blockIdx.x;
-  const int per = total_wg / 8;
-  const int logical = (wg < per * 8) ? (wg % 8) * per + wg / 8 : wg;
+  const int logical = tile_order(wg, total_wg);
   const int tile = ntiles - 1 - logical % ntiles;
   const int g = (logical / ntiles) % h_kv;
   const int b = logical / (ntiles * h_kv);
