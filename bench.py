@@ -144,9 +144,9 @@ def kernel_src_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kind: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary of this workload, if it was taken on the current attention kernel sources."""
+def load_counters(workload: str, kind: str):
+    """The committed rocprofv3 counter summary of this workload's attention launch, if it was
+    taken on the current attention kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -154,7 +154,39 @@ def load_traffic(workload: str, kind: str):
         t = json.load(f)
     if t.get("kernel_src_sha") != kernel_src_hash(kind):
         return None
-    return t.get("bytes_per_launch")
+    return t
+
+
+def prefill_tile_shape(h_q: int, h_kv: int, d: int):
+    """(positions per workgroup tile, positions per wave) of the bf16 prefill kernels."""
+    g = h_q // h_kv
+    pw = 32 // g if d <= 128 else (16 * (2 if g == 32 else 1)) // g
+    return 8 * pw, pw
+
+
+def union_stats(sel, pos, block: int, mq: int, pw: int):
+    """Lock-step work of the prefill kernels from a selection: a tile of mq consecutive rows
+    walks the union of its rows' selected blocks and own (non-empty trailing) blocks, a wave of
+    pw rows computes on the union of its rows'.  sel [n_q, k] (-1 padded) and pos [n_q] (row
+    positions; negative = padding) of one sequence.  Returns (sum over tiles of union x rows,
+    same over waves, sum over rows of blocks needed)."""
+    import numpy as np
+    n = np.where(pos >= 0, (pos + 1) // block, 0)
+    valid = (sel >= 0) & (sel < n[:, None]) & (pos >= 0)[:, None]
+    own = np.where((pos >= 0) & ((pos + 1) % block != 0), pos // block, -1)
+    needed = int(valid.sum() + (own >= 0).sum())
+
+    def walked(step):
+        tot = 0
+        for a in range(0, len(pos), step):
+            rows = slice(a, a + step)
+            live = int((pos[rows] >= 0).sum())
+            if live:
+                u = np.union1d(sel[rows][valid[rows]], own[rows][own[rows] >= 0])
+                tot += len(u) * live
+        return tot
+
+    return walked(mq), walked(pw), needed
 
 
 # ---------------------------------------------------------------------------
@@ -377,7 +409,11 @@ def main():
         achieved = work / (att_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = load_traffic(w.name, w.kind)
+    counters = load_counters(w.name, w.kind)
+    roof["traffic"] = counters.get("bytes_per_launch") if counters else None
+    if counters and "mfma" in counters:
+        roof["mfma_executed_over_algorithmic"] = counters["mfma"]["executed_over_algorithmic"]
+        roof["mfma_busy_pct"] = counters["mfma"]["busy_pct"]
     # the attention call: one kernel for prefill; split kernel + merge kernel for decode
     roof["kernel"] = (("qsa::prefill_bf16_rt_kernel" if w.d == 256 else "qsa::prefill_bf16_kernel")
                       if w.kind in ("prefill", "varlen")
@@ -401,6 +437,21 @@ def main():
                    prompt_len_max=int(lens.max()), prompt_tokens=int(lens.sum()))
     else:
         cfg.update(max_len=w.max_len, kv_len_min=int(lens.min()), kv_len_max=int(lens.max()))
+    if w.kind in ("prefill", "varlen") and w.dtype == "bf16":
+        # blocks the kernel walks per row (tile union) and computes on (wave union), over the
+        # blocks a row needs, from this run's own selection
+        sel = plan.sel.cpu().numpy()
+        n_q = sel.shape[1]
+        mq, pw = prefill_tile_shape(w.h_q, w.h_kv, w.d)
+        kvl = lens if w.kind == "varlen" else [w.seq] * sel.shape[0]
+        tt = wv = nd = 0
+        for b in range(sel.shape[0]):
+            a, c, e = union_stats(sel[b], np.arange(n_q) + int(kvl[b]) - n_q, w.block, mq, pw)
+            tt, wv, nd = tt + a, wv + c, nd + e
+        roof["union"] = {"tile_positions": mq, "wave_positions": pw,
+                         "tile_over_needed": round(tt / max(nd, 1), 3),
+                         "wave_over_needed": round(wv / max(nd, 1), 3)}
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
