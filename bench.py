@@ -311,7 +311,7 @@ def cpu_baseline(w, inps, lens, budget_s: float):
             sample = (f"{done} of {w.batch} sequences (selection + attention per new token; the "
                       f"compressed indexer state is prepared untimed, as on the GPU)")
     return {"value": round(value, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": sample}
+            "sample": sample, "host_cpus": os.cpu_count(), "blas_threads": 1}
 
 
 # ---------------------------------------------------------------------------
