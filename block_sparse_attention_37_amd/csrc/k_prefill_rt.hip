@@ -100,6 +100,10 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
   const int words = p_hi >= 0 ? (p_hi / block) / 32 + 1 : 0;
 
   const int tid = threadIdx.x;
+  if (p_hi < 0) {  // padding rows only
+    write_padding_tile<D, G>(out, lse, b, n_q, h_q, g, q0, min(MQ, n_q - q0), tid, NT);
+    return;
+  }
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
 

@@ -52,6 +52,31 @@ __device__ __forceinline__ int tile_order(int wg, int total) {
   return (k / kTileRun) * 8 * kTileRun + xcd * kTileRun + k % kTileRun;
 }
 
+// A tile whose rows are all padding (p < 0 for every row: its sequence is shorter than n_q)
+// writes zeros to its output rows and -inf to their log-sum-exp, the values the full path
+// gives such rows, and the workgroup leaves without loading anything.  Rows q0 .. q0+rows-1
+// of sequence b, query heads g*G .. g*G+G-1 (contiguous in a row: G*D bf16, 16-byte units;
+// the entry points require 16-byte aligned tensors).  No barrier: a workgroup-uniform
+// early exit.
+template <int D, int G>
+__device__ __forceinline__ void write_padding_tile(uint16_t* __restrict__ out,
+                                                   float* __restrict__ lse, int b, int n_q,
+                                                   int h_q, int g, int q0, int rows, int tid,
+                                                   int nthreads) {
+  constexpr int UPR = G * D / 8;  // 16-byte units per query position
+  uint16_t* base = out + (((size_t)b * n_q + q0) * h_q + g * G) * D;
+  for (int e = tid; e < rows * UPR; e += nthreads) {
+    const int r = e / UPR;
+    *reinterpret_cast<u32x4*>(base + (size_t)r * h_q * D + (e - r * UPR) * 8) = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (lse) {
+    for (int e = tid; e < rows * G; e += nthreads) {
+      const int r = e / G;
+      lse[((size_t)b * n_q + q0 + r) * h_q + g * G + (e - r * G)] = -__builtin_inff();
+    }
+  }
+}
+
 // Instruction-order hints for the scheduler (no effect on results): mask selects the
 // instruction class (0x8 MFMA, 0x100 LDS read), n how many of them come next.
 template <int MASK, int N>

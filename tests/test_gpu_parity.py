@@ -194,7 +194,11 @@ def test_prefill_varlen(gpu, case):
     kvl = torch.tensor(lens, dtype=torch.int32, device=gpu)
     cmp = Q.compress_keys(ik, B, kv_lens=kvl)
     sel = Q.index_topk(iq, cmp, B, w.top_k, kv_lens=kvl)
-    out, lse = Q.sparse_attn_prefill_varlen(q, k, v, kvl, sel, B, w.sm_scale, return_lse=True)
+    # outputs start as NaN: every row, padding included, must be written by the kernels
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((nb, n_q, w.h_q), float("nan"), dtype=torch.float32, device=gpu)
+    out, lse = Q.sparse_attn_prefill_varlen(q, k, v, kvl, sel, B, w.sm_scale, return_lse=True,
+                                            out=out, lse=lse)
     torch.cuda.synchronize()
     sel_n, out_n, lse_n = sel.cpu().numpy(), out.float().cpu().numpy(), lse.cpu().numpy()
     worst = 0.0
