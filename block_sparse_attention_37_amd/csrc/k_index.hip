@@ -135,12 +135,23 @@ __global__ __launch_bounds__(256) void index_topk_kernel(
   const int len = kv_lens ? kv_lens[b] : n_q;
   const int nq_here = min(QT, n_q - i0);
   const int cap = min(max_blocks, NC);
+  // query qi sits at position p0 + qi; positions < 0 are padding (a sequence shorter than
+  // n_q): no candidates, so their rows are all -1
+  const int p0 = len - n_q + i0;
+  if (p0 + nq_here - 1 < 0) {  // padding only: no loads, no barrier
+    for (int e = tid; e < nq_here * top_k; e += 256) {
+      const size_t o = ((size_t)b * n_q + i0) * top_k + e;
+      sel[o] = -1;
+      if (sel_scores) sel_scores[o] = -__builtin_inff();
+    }
+    return;
+  }
 
-  // 1. head-summed indexer queries
+  // 1. head-summed indexer queries (zero for padding rows, which score nothing)
   for (int e = tid; e < QT * d_idx; e += 256) {
     const int qi = e / d_idx, c = e % d_idx;
     float s = 0.f;
-    if (qi < nq_here) {
+    if (qi < nq_here && p0 + qi >= 0) {
       const T* src = iq + ((size_t)b * n_q + i0 + qi) * h_idx * d_idx + c;
       for (int h = 0; h < h_idx; ++h) s += Elem<T>::load(src, (size_t)h * d_idx);
     }
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(
   __syncthreads();
 
   // 2. scores of candidate blocks (the last query of the tile sees the most)
-  const int p_last = len - n_q + i0 + nq_here - 1;
+  const int p_last = p0 + nq_here - 1;
   const int n_last = max(0, min((p_last + 1) / block, cap));
   for (int j = tid; j < n_last; j += 256) {
     const float* row = cmp + ((size_t)b * max_blocks + j) * d_idx;
@@ -173,7 +184,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   for (int qi = wave; qi < nq_here; qi += 4) {
-    const int p = len - n_q + i0 + qi;
+    const int p = p0 + qi;
     const int n = max(0, min((p + 1) / block, cap));
     const size_t orow = ((size_t)b * n_q + i0 + qi) * top_k;
     select_topk_wave<NR>(sc[qi], n, top_k, lane, sel + orow, sel_scores ? sel_scores + orow : nullptr);
