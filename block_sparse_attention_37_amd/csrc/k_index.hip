@@ -118,6 +118,21 @@ __device__ __forceinline__ void select_topk_wave(const float* sc, int n, int top
   }
 }
 
+// acc[k] += element k of a 16-byte load of T values (8 bf16 or 4 float).
+template <typename T>
+__device__ __forceinline__ void add_row16(float* acc, const u32x4& v) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc[2 * w] += bf16_to_f32(v[w] & 0xffffu);
+      acc[2 * w + 1] += bf16_to_f32(v[w] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc[w] += __uint_as_float(v[w]);
+  }
+}
+
 }  // namespace
 
 template <typename T, int NR, int QT>
@@ -147,15 +162,33 @@ __global__ __launch_bounds__(256) void index_topk_kernel(
     return;
   }
 
-  // 1. head-summed indexer queries (zero for padding rows, which score nothing)
-  for (int e = tid; e < QT * d_idx; e += 256) {
-    const int qi = e / d_idx, c = e % d_idx;
-    float s = 0.f;
-    if (qi < nq_here && p0 + qi >= 0) {
-      const T* src = iq + ((size_t)b * n_q + i0 + qi) * h_idx * d_idx + c;
-      for (int h = 0; h < h_idx; ++h) s += Elem<T>::load(src, (size_t)h * d_idx);
+  // 1. head-summed indexer queries (zero for padding rows, which score nothing).  The QT
+  // queries' indexer rows are one contiguous [QT][h_idx][d_idx] slab; a lane owns CPT
+  // consecutive dims of one query and adds its heads in order from 16-byte loads, eight
+  // heads in flight at a time.
+  {
+    constexpr int CPT = 16 / sizeof(T);
+    const int lanes_per_q = d_idx / CPT;
+    if (tid < QT * lanes_per_q) {
+      const int qi = tid / lanes_per_q, c0 = (tid % lanes_per_q) * CPT;
+      float acc[CPT];
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) acc[k] = 0.f;
+      if (qi < nq_here && p0 + qi >= 0) {
+        const T* src = iq + ((size_t)b * n_q + i0 + qi) * h_idx * d_idx + c0;
+        int h = 0;
+        for (; h + 8 <= h_idx; h += 8) {
+          u32x4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(h + u) * d_idx);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) add_row16<T>(acc, v[u]);
+        }
+        for (; h < h_idx; ++h) add_row16<T>(acc, *reinterpret_cast<const u32x4*>(src + (size_t)h * d_idx));
+      }
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) qs[c0 + k][qi] = acc[k];
     }
-    qs[c][qi] = s;
   }
   __syncthreads();
 
