@@ -195,18 +195,23 @@ __global__ __launch_bounds__(256) void index_topk_kernel(
   // 2. scores of candidate blocks (the last query of the tile sees the most)
   const int p_last = p0 + nq_here - 1;
   const int n_last = max(0, min((p_last + 1) / block, cap));
+  // One row per lane and pass, 16 dims (four 16-byte loads) at a time.
   for (int j = tid; j < n_last; j += 256) {
     const float* row = cmp + ((size_t)b * max_blocks + j) * d_idx;
     float acc[QT];
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi) acc[qi] = 0.f;
-    for (int c = 0; c < d_idx; c += 4) {
-      const f32x4 kv = *reinterpret_cast<const f32x4*>(row + c);
+    for (int c0 = 0; c0 < d_idx; c0 += 16) {
+      f32x4 kv[4];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
+      for (int t = 0; t < 4; ++t) kv[t] = *reinterpret_cast<const f32x4*>(row + c0 + 4 * t);
 #pragma unroll
-        for (int qi = 0; qi < QT; ++qi) acc[qi] = __builtin_fmaf(qs[c + cc][qi], kv[cc], acc[qi]);
-      }
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int qi = 0; qi < QT; ++qi)
+            acc[qi] = __builtin_fmaf(qs[c0 + 4 * t + cc][qi], kv[t][cc], acc[qi]);
     }
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi) sc[qi][j] = acc[qi];
