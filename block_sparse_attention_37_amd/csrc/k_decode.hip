@@ -84,6 +84,19 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(
   const int n = len / block;
   const int ntrail = len - n * block;
 
+  // query rows: lane holds row nr = lane & 15 (query head g*G + nr when nr < G).  The Q
+  // loads are issued before the selection is read, so the two latencies overlap.
+  const int nr = lane & 15;
+  const int quarter = lane >> 4;
+  u32x4 qraw[NQT];
+  {
+    const bool ok = nr < G;
+    const uint16_t* qp = q + ((size_t)b * h_q + g * G + (ok ? nr : 0)) * D + quarter * 8;
+#pragma unroll
+    for (int t = 0; t < NQT; ++t)
+      qraw[t] = ok ? *reinterpret_cast<const u32x4*>(qp + t * 32) : u32x4{0u, 0u, 0u, 0u};
+  }
+
   // compact the valid selected blocks (0 <= j < n), keeping their order
   if (wave == 0) {
     int base = 0;
@@ -99,6 +112,14 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(
     if (lane == 0) list_n = base;
   }
   __syncthreads();
+  bf16x8 qreg[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    // opaque to the optimizer: Q stays in registers (a re-load inside the loop would also
+    // wait for the key/value loads in flight); its wait comes before those loads are issued
+    keep_in_register(qraw[t]);
+    qreg[t] = bitcast<bf16x8>(qraw[t]);
+  }
   const int mv = list_n;
   const int nsub = (block + KC - 1) / KC;
   const int tunits = (ntrail + KC - 1) / KC;
@@ -146,23 +167,6 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(
 
   int issued = 0;
   for (; issued < NS - 1 && issued < nch; ++issued) issue(c_begin + issued);
-
-  // query rows: lane holds row nr = lane & 15 (query head g*G + nr when nr < G)
-  const int nr = lane & 15;
-  const int quarter = lane >> 4;
-  bf16x8 qreg[NQT];
-  {
-    const bool ok = nr < G;
-    const uint16_t* qp = q + ((size_t)b * h_q + g * G + (ok ? nr : 0)) * D + quarter * 8;
-#pragma unroll
-    for (int t = 0; t < NQT; ++t) {
-      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qp + t * 32) : u32x4{0u, 0u, 0u, 0u};
-      // opaque to the optimizer: Q stays in registers (a re-load inside the loop would also
-      // wait for the key/value loads in flight)
-      keep_in_register(w);
-      qreg[t] = bitcast<bf16x8>(w);
-    }
-  }
 
   float m_run = -__builtin_inff();
   float l_run = 0.f;
