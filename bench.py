@@ -318,8 +318,8 @@ def cpu_baseline(w, inps, lens, budget_s: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this QSA build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "QSA here runs on exactly one GPU; --gpus must be 1 "
+                                   "(sharding across GPUs is not implemented)"}))
         return 2
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
