@@ -99,6 +99,10 @@ EDGE_PREFILL = [
     _wl("d256_g32", seq=50, block=16, top_k=2, h_q=32, h_kv=1, d=256),
     _wl("d256_g16_block100", seq=260, block=100, top_k=1, h_q=16, h_kv=1, d=256),
     _wl("f32_d256", seq=40, block=16, top_k=2, h_q=4, h_kv=2, d=256, dtype="f32"),
+    # indexer head sum: eight heads per load round plus a tail, narrow and wide indexer dims
+    _wl("hidx12_didx32", seq=500, block=32, top_k=4, h_q=8, h_kv=2, d=128, h_idx=12, d_idx=32),
+    _wl("f32_hidx9_didx128", seq=120, block=8, top_k=3, h_q=4, h_kv=2, d=64, h_idx=9, d_idx=128,
+        dtype="f32"),
 ]
 
 
