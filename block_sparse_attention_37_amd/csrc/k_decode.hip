@@ -304,23 +304,26 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   if (lse && d == 0) lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
-bool decode_bf16_supported(int group, int d, int block, int top_k) {
+bool decode_bf16_supported(int group, int d, int block, int top_k, int max_len, int h_kv) {
   if (d != 64 && d != 128 && d != 256) return false;
   if (group < 1 || group > 16) return false;
+  // element offsets of K / V rows within one sequence's cache are 32-bit
+  if ((long long)max_len * h_kv * d >= (1ll << 32)) return false;
   return block >= 1 && block <= 1024 && top_k >= 1 && top_k <= kMaxTopK;
 }
 
-// Workgroups that run at once: one per CU (the LDS ring takes 128 KB at D = 128).
+// Workgroups that run at once: one per CU (the LDS ring takes 128 KB at D = 128).  The count
+// is read from the device current at the first call; the initialisation of a function-local
+// static is thread-safe, so concurrent first calls from several host threads agree.
 static int decode_slots() {
-  static int slots = 0;
-  if (slots == 0) {
+  static const int slots = [] {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    slots = cus;
-  }
+    return cus;
+  }();
   return slots;
 }
 

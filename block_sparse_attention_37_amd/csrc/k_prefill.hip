@@ -62,8 +62,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ sel, uint16_t* __restrict__ out,
     float* __restrict__ lse, int n_q, int kv_len_all, int h_q, int h_kv, int block, int top_k,
-    float scale_log2, int ntiles, int total_wg, const int32_t* __restrict__ kv_lens,
-    int kv_stride) {
+    float scale_log2, uint32_t q_and, uint32_t q_xor, int ntiles, int total_wg,
+    const int32_t* __restrict__ kv_lens, int kv_stride) {
   constexpr int NT = NW * 64;
   constexpr int PW = 32 / G;       // positions per wave
   constexpr int MQ = NW * PW;      // positions per workgroup
@@ -129,15 +129,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   }
 
   // ---- selection rows of the tile -> LDS; union bitmap ----
-  for (int e = tid; e < MQ * top_k; e += NT) {
-    const int pos = e / top_k;
-    const int p = p0 + pos;
-    uint16_t j = kNoSel;
-    if (p >= 0 && p < kv_len) {
-      const int jj = sel[((size_t)b * n_q + q0 + pos) * top_k + (e - pos * top_k)];
-      if (jj >= 0 && jj < (p + 1) / block) j = (uint16_t)jj;
+  // Each row is compacted to its ids in [0, n(p)) in their given order, then kNoSel
+  // (one wave per row, ballot prefix counts), so the walk below never stops at an ignored id.
+  for (int r = wave; r < MQ; r += NW) {
+    const int pr = p0 + r;
+    const bool live = pr >= 0 && pr < kv_len;
+    const int np = live ? (pr + 1) / block : 0;
+    const int32_t* srow = sel + ((size_t)b * n_q + q0 + r) * top_k;
+    int base = 0;
+    for (int e0 = 0; e0 < top_k; e0 += 64) {
+      const int e = e0 + lane;
+      const int jj = (live && e < top_k) ? srow[e] : -1;
+      const bool ok = jj >= 0 && jj < np;
+      const uint64_t m = __ballot(ok);
+      if (ok) sel_s[r * top_k + base + __popcll(m & lanemask_lt())] = (uint16_t)jj;
+      base += __popcll(m);
     }
-    sel_s[e] = j;
+    for (int e = base + lane; e < top_k; e += 64) sel_s[r * top_k + e] = kNoSel;
   }
   for (int w = tid; w < max(words, 1); w += NT) bm[w] = 0u;
   __syncthreads();
@@ -159,6 +167,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   for (int t = 0; t < NKS; ++t) {
     // opaque to the optimizer: keeps Q in registers instead of re-loading it per chunk
     // (a re-load would also wait on the untracked K/V loads in flight)
+    qraw[t] = (qraw[t] & q_and) ^ q_xor;  // sign of the scale (PrefillScale)
     keep_in_register(qraw[t]);
     qreg[t] = bitcast<bf16x8>(qraw[t]);
   }
@@ -481,11 +490,12 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
   const int ntiles = (n_q + MQ - 1) / MQ;
   const long long total = (long long)ntiles * h_kv * batch;
   if (total > INT_MAX) return hipErrorInvalidValue;
+  const PrefillScale sc = prefill_scale(sm_scale, kLog2e);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, G>), dim3((unsigned)total), dim3(NW * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse, n_q,
-                     kv_len, h_q, h_kv, block, top_k, sm_scale * kLog2e, ntiles, (int)total,
-                     kv_lens, kv_stride);
+                     kv_len, h_q, h_kv, block, top_k, sc.scale_log2, sc.q_and, sc.q_xor, ntiles,
+                     (int)total, kv_lens, kv_stride);
   return hipGetLastError();
 }
 

@@ -77,6 +77,25 @@ __device__ __forceinline__ void write_padding_tile(uint16_t* __restrict__ out,
   }
 }
 
+// The softmax scale as the prefill kernels apply it.  They take the row maximum of the raw
+// scores and fold the scale into one FMA per score afterwards, which needs a positive scale:
+// a negative scale would turn the maximum into the minimum, and a zero scale would multiply
+// the -inf of masked keys by 0.  The sign goes into Q instead, exactly: S = K.(-Q)^T is -S
+// bit for bit (every product changes sign, the sums round symmetrically), so a negative
+// scale flips the sign bit of every bf16 element of Q and uses |scale|.  A zero scale gives
+// every visible key the same weight: Q is zeroed (every score is exactly 0) and the scale
+// is 1, so masked keys keep -inf.
+struct PrefillScale {
+  float scale_log2;  // positive scale in log2 units
+  uint32_t q_and;    // applied to each 32-bit pair of bf16 Q elements: (x & q_and) ^ q_xor
+  uint32_t q_xor;
+};
+inline PrefillScale prefill_scale(float sm_scale, float log2e) {
+  if (sm_scale == 0.0f) return {1.0f, 0u, 0u};
+  if (sm_scale < 0.0f) return {-sm_scale * log2e, 0xFFFFFFFFu, 0x80008000u};
+  return {sm_scale * log2e, 0xFFFFFFFFu, 0u};
+}
+
 // Instruction-order hints for the scheduler (no effect on results): mask selects the
 // instruction class (0x8 MFMA, 0x100 LDS read), n how many of them come next.
 template <int MASK, int N>

@@ -255,8 +255,10 @@ qsa_status qsa_sparse_attn_decode(const void* q, const void* k_cache, const void
   QSA_PTR(out, "out");
   QSA_OPT_PTR(lse, "lse");
   if (dt == QSA_BF16) {
-    QSA_REQUIRE(qsa::decode_bf16_supported(h_q / h_kv, d, block, top_k), QSA_ERR_UNSUPPORTED,
-                "bf16 decode not built for group %d, d %d", h_q / h_kv, d);
+    QSA_REQUIRE(qsa::decode_bf16_supported(h_q / h_kv, d, block, top_k, max_len, h_kv),
+                QSA_ERR_UNSUPPORTED,
+                "bf16 decode not built for group %d, d %d, max_len %d, h_kv %d", h_q / h_kv, d,
+                max_len, h_kv);
     const int ns = qsa::decode_num_splits(batch, h_kv, block, top_k);
     const size_t need = qsa::decode_workspace_bytes(batch, h_q, d, ns);
     QSA_REQUIRE(workspace_bytes >= need, QSA_ERR_INVALID_ARGUMENT,

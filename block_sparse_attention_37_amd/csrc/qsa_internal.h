@@ -56,7 +56,7 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const
                            int top_k, float sm_scale, hipStream_t stream);
 
 // bf16 decode on matrix cores, split over chunks of the selected tokens.
-bool decode_bf16_supported(int group, int d, int block, int top_k);
+bool decode_bf16_supported(int group, int d, int block, int top_k, int max_len, int h_kv);
 int decode_num_splits(int batch, int h_kv, int block, int top_k);
 size_t decode_workspace_bytes(int batch, int h_q, int d, int nsplit);
 hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache,

@@ -159,13 +159,15 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
  *
  *   q, out   [batch, seq, h_q, d]   element type dt (out may not alias any input)
  *   k, v     [batch, seq, h_kv, d]  element type dt
- *   sel      [batch, seq, top_k] int32: per row, strictly ascending block ids < n(p)
- *            followed by -1 padding (exactly what qsa_index_topk writes); ids outside
- *            [0, n(p)) are ignored
+ *   sel      [batch, seq, top_k] int32: per row, block ids < n(p) followed by -1 padding
+ *            (exactly what qsa_index_topk writes); ids outside [0, n(p)) are ignored
+ *            wherever they stand, and the ids inside it must be strictly ascending
  *   lse      [batch, seq, h_q] float32 output or NULL
- * Invalid: h_q % h_kv != 0.  bf16 computes Q.K^T and P.V on bf16 matrix cores with
- * float32 accumulation and float32 softmax (P rounded to bf16), out rounded to nearest
- * even; f32 computes everything in float32.
+ * Invalid: h_q % h_kv != 0, a non-finite sm_scale.  Any finite sm_scale is accepted (a
+ * negative one ranks keys in reverse, zero gives every token of T(p) the same weight).
+ * bf16 computes Q.K^T and P.V on bf16 matrix cores with float32 accumulation and float32
+ * softmax (P rounded to bf16), out rounded to nearest even; f32 computes everything in
+ * float32.
  * Supported: d in {64, 128, 256} (256: the model page's default attention shape);
  * top_k <= 256; block in [1, 1024].  bf16 also needs G = h_q / h_kv in {1, 2, 4, 8, 16, 32},
  * T * top_k <= 8192 where T = 256 / G positions per tile for d <= 128 and
@@ -248,8 +250,8 @@ qsa_status qsa_sparse_attn_decode_workspace_size(int batch, int h_q, int h_kv, i
  *                     allowed when that size is 0); contents need no initialization and
  *                     are scratch: two calls in flight at once must not share it
  * Invalid: h_q % h_kv != 0, workspace_bytes too small.
- * Supported: d in {64, 128, 256}; bf16 needs h_q / h_kv in {1, 2, 4, 8, 16}; top_k <= 256;
- * block in [1, 1024].
+ * Supported: d in {64, 128, 256}; bf16 needs h_q / h_kv in {1, 2, 4, 8, 16} and
+ * max_len * h_kv * d < 2^32; top_k <= 256; block in [1, 1024].
  */
 qsa_status qsa_sparse_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* kv_lens, const int32_t* sel,
