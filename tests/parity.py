@@ -12,6 +12,8 @@ inside a tie band cannot fail the attention check).
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 import oracle.qsa_oracle as O
@@ -75,3 +77,37 @@ def max_abs(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def stratified_rows(T, block, top_k, total, seed):
+    """Query rows for attention parity at full size: rows 0 .. 2*block-1 (short token sets,
+    the first block ends), every block-end row ((p+1) % block == 0) in the last 8 blocks,
+    the last two rows, then seeded rows drawn uniformly from the rows with a full selection
+    (n(p) >= top_k, so |T(p)| >= top_k*block) until there are ``total`` rows."""
+    rows = set(range(min(T, 2 * block)))
+    rows |= {p for p in range(max(0, T - 8 * block), T) if (p + 1) % block == 0}
+    rows |= {p for p in (T - 1, T - 2) if p >= 0}
+    lo = min(max(top_k * block - 1, 0), T - 1)
+    pool = np.setdiff1d(np.arange(lo, T), np.fromiter(rows, dtype=np.int64))
+    need = max(0, min(total - len(rows), len(pool)))
+    rows |= set(np.random.default_rng(seed).choice(pool, size=need, replace=False).tolist())
+    return sorted(rows)
+
+
+def attend_rows_threaded(q, k, v, sel, positions, rows, block, sm_scale, threads=8):
+    """oracle.attend_rows over ``rows``, split across threads (NumPy releases the GIL in the
+    gathers and products; BLAS is held to one thread per call).  Same results as one call."""
+    from threadpoolctl import threadpool_limits
+    rows = list(rows)
+    if not rows:
+        return O.attend_rows(q, k, v, sel, positions, rows, block, sm_scale)
+    parts = [rows[i::threads] for i in range(threads) if rows[i::threads]]
+    with threadpool_limits(limits=1), ThreadPoolExecutor(len(parts)) as ex:
+        res = list(ex.map(lambda r: O.attend_rows(q, k, v, sel, positions, r, block, sm_scale),
+                          parts))
+    out = np.zeros((len(rows),) + res[0][0].shape[1:], dtype=np.float64)
+    lse = np.zeros((len(rows),) + res[0][1].shape[1:], dtype=np.float64)
+    for i, (o, l) in enumerate(res):
+        out[i::threads] = o
+        lse[i::threads] = l
+    return out, lse
