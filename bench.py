@@ -2,8 +2,10 @@
 """QSA throughput on one MI355X: one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--graph | --no-graph] [--no-cpu-baseline]
+                    [--graph | --no-graph] [--no-cpu-baseline] [--no-calibration]
     python bench.py --calibrate-copy MIB
+    python bench.py --calibrate-read MIB
+    python bench.py --calibrate-mfma
 
 
 A step is one pass of the whole QSA path over one batch of synthetic input:
@@ -19,24 +21,33 @@ A step is one pass of the whole QSA path over one batch of synthetic input:
 Inputs are resident in HBM before the timed region starts.  ``value`` is
 tokens/s of the whole step (prefill: batch*seq tokens, varlen: the prompts' tokens,
 decode: batch tokens).  With ``--graph`` (the default) the steps are launched from a
-HIP graph that holds ``steps_per_graph`` consecutive whole steps (the largest divisor
-of K up to 16), replayed K / steps_per_graph times: every timed step runs all of its
-kernels, in stream order; only the fixed cost of launching a graph is shared.
+HIP graph that holds ``steps_per_graph`` consecutive whole steps, replayed
+K / steps_per_graph times (at least 20 replays when K allows it): every timed step runs
+all of its kernels, in stream order; only the fixed cost of launching a graph is shared.
+Each replay is bracketed by its own pair of events; ``ms_per_step`` is the median replay
+time per step (the mean is reported beside it).
 
 ``roofline`` describes the dominant kernel (the attention kernel): algorithmic
 flops (prefill, bf16 matrix cores) or algorithmic bytes (decode, HBM) per launch
-divided by its average launch time, measured with events recorded on the stream
-the kernels run on around `steps` back-to-back attention calls that follow the
-timed steps.  ``traffic`` is the HBM byte count per launch from the committed
-profiler counter summary of the workload (null when the attention kernel's sources
-changed since it was taken).
+divided by its median launch time, measured with events recorded on the stream the
+kernels run on around each of >= 20 replays of back-to-back attention calls that follow
+the timed steps.  ``frac`` is against the vendor peak, ``frac_of_measured`` against the
+rate the calibration kernel of the same resource sustains in the same run
+(``--no-calibration`` skips it).  ``traffic`` is the HBM byte count per launch from the
+committed profiler counter summary of the workload (null when the attention kernel's
+sources changed since it was taken); ``traffic_over_compulsory`` divides it by the bytes
+the launch must move at least once (every input read once, every output written once).
 ``cpu_baseline`` times the fp64 oracle (single-threaded BLAS) on a bounded
-sample of the same workload.
+sample of the same workload; ``tie_band_rows`` is the fraction of that sample's
+selection rows whose m-th and (m+1)-th oracle scores lie within 1e-3 relative.
 
 ``--calibrate-copy MIB`` runs only a plain device copy of MIB MiB (one
 elementwise kernel that reads and writes MIB MiB, five launches): the byte
 counters of the profiler (FETCH_SIZE, WRITE_SIZE) read on it give the scale
 factors that turn the counters of the attention kernels into bytes.
+``--calibrate-read MIB`` / ``--calibrate-mfma`` run only the calibration kernels
+(libqsa_calib.so: a streaming read of MIB MiB, a dense bf16 MFMA loop) and print their
+rates, for profiler summaries of the measured peaks.
 """
 from __future__ import annotations
 
@@ -55,7 +66,7 @@ sys.path.insert(0, ROOT)
 METRIC = "QSA tokens/s (prefill & decode, 1 GPU); % of HBM / bf16 MFMA roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
-DEFAULT_WORKLOAD = "prefill_bf16_4k"
+DEFAULT_WORKLOAD = "long_prefill_bf16_128k"
 
 
 def parse():
@@ -73,6 +84,12 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--calibrate-read", type=int, default=0, metavar="MIB",
+                    help="run only the streaming-read calibration kernel over MIB MiB")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="run only the dense bf16 MFMA calibration kernel")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the measured-peak calibration of the default run")
     return ap.parse_args()
 
 
@@ -117,9 +134,33 @@ def decode_attention_bytes(w, lens) -> float:
     return kv + 2.0 * w.batch * w.h_q * w.d * esz + w.batch * w.top_k * 4 + w.batch * 4
 
 
-def graph_steps(steps: int, most: int = 16) -> int:
-    """Steps captured in one graph: the largest divisor of `steps` up to `most`."""
-    return max(d for d in range(1, min(most, steps) + 1) if steps % d == 0)
+def graph_steps(steps: int, most: int = 16, replays: int = 20) -> int:
+    """Steps captured in one graph: the largest divisor of `steps` up to `most` that still
+    leaves at least `replays` replays (all `steps` replays when there are fewer steps)."""
+    need = min(replays, steps)
+    return max(d for d in range(1, min(most, steps) + 1) if steps % d == 0 and steps // d >= need)
+
+
+def median_ms(pairs) -> tuple:
+    """(median, mean) of the elapsed times of (start, end) event pairs, in ms."""
+    t = sorted(a.elapsed_time(b) for a, b in pairs)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    return med, sum(t) / n
+
+
+def compulsory_bytes(w, lens=None) -> float:
+    """Bytes a prefill attention launch moves at least once: q, k, v and sel read, out and
+    lse written (varlen: each prompt's own rows)."""
+    esz = 2 if w.dtype == "bf16" else 4
+    if lens is not None:
+        rows = float(np.sum(lens))
+        kv_rows = rows
+    else:
+        rows = float(w.batch * (w.n_q or w.seq))
+        kv_rows = float(w.batch * w.seq)
+    per_row = w.h_q * w.d * esz * 2 + w.top_k * 4 + w.h_q * 4  # q + out + sel + lse
+    return rows * per_row + kv_rows * w.h_kv * w.d * esz * 2
 
 
 # Sources the attention kernel of each workload kind is compiled from (with the build
@@ -256,12 +297,38 @@ def setup_decode(w, dev):
 
 
 # ---------------------------------------------------------------------------
+def _tie_band(scores, top_k: int, rel: float = 1e-3) -> bool:
+    """True when the m-th and (m+1)-th largest scores of a row lie within `rel` relative
+    (m = min(top_k, n); rows that keep every candidate have no band)."""
+    n = len(scores)
+    m = min(top_k, n)
+    if m == n:
+        return False
+    srt = np.sort(scores)[::-1]
+    a, b = srt[m - 1], srt[m]
+    scale = max(abs(a), abs(b))
+    return scale > 0 and (a - b) / scale <= rel
+
+
+def baseline_rows(T: int, block: int, top_k: int, seed: int = 0):
+    """Stratified oracle sample of a prompt: the first 2*block rows, the block-end rows of the
+    last 8 blocks, the last row, then seeded rows drawn uniformly from the whole prompt (in
+    that order, so a time budget cuts the seeded tail)."""
+    head = list(range(min(T, 2 * block)))
+    ends = [p for p in range(max(2 * block, T - 8 * block), T) if (p + 1) % block == 0]
+    last = [T - 1] if T - 1 not in head and T - 1 not in ends else []
+    fixed = set(head) | set(ends) | set(last)
+    rest = [int(p) for p in np.random.default_rng(seed).permutation(T) if int(p) not in fixed]
+    return head, ends + last, rest
+
+
 def cpu_baseline(w, inps, lens, budget_s: float):
     """The fp64 oracle on a bounded sample of the workload, single-threaded BLAS."""
     from threadpoolctl import threadpool_limits
     import oracle.qsa_oracle as O
     from block_sparse_attention_37_amd import synth as S
     t_start = time.perf_counter()
+    ties = rows_scored = 0
     with threadpool_limits(limits=1):
         if w.kind in ("prefill", "varlen"):
             if w.kind == "varlen":  # the longest prompt of the batch stands for the others
@@ -275,43 +342,68 @@ def cpu_baseline(w, inps, lens, budget_s: float):
             cmp = O.compress_keys(ik, w.block)
             t_cmp = time.perf_counter() - t0
             nq = w.n_q or w.seq
-            rows = w.seq - nq + np.random.default_rng(0).permutation(nq)
-            done, t_rows = 0, 0.0
-            for p in rows:
-                t0 = time.perf_counter()
-                n = O.candidate_blocks(int(p), w.block)
-                s = O.block_scores(iq[p], cmp, n)
-                sel = O.select_blocks(s, w.top_k)
-                O.attend(q[p], k, v, O.token_set(sel, int(p), w.block), w.sm_scale)
-                t_rows += time.perf_counter() - t0
-                done += 1
-                if time.perf_counter() - t_start > budget_s:
-                    break
-            per_tok = t_rows / done + t_cmp / nq
-            sample = (f"compression of all {w.seq} tokens + selection and attention of {done} "
-                      f"randomly chosen query rows of {nq}; tokens/s extrapolated per row")
+            lo = w.seq - nq
+            head, ends, rest = baseline_rows(nq, w.block, w.top_k)
+            timed = {}
+            for part, rows in (("head", head), ("ends", ends), ("uniform", rest)):
+                for i in rows:
+                    p = lo + i
+                    t0 = time.perf_counter()
+                    n = O.candidate_blocks(int(p), w.block)
+                    s = O.block_scores(iq[p], cmp, n)
+                    sel = O.select_blocks(s, w.top_k)
+                    O.attend(q[p], k, v, O.token_set(sel, int(p), w.block), w.sm_scale)
+                    timed.setdefault(part, []).append(time.perf_counter() - t0)
+                    ties += int(_tie_band(s, w.top_k))
+                    rows_scored += 1
+                    if part == "uniform" and time.perf_counter() - t_start > budget_s:
+                        break
+            # the uniform rows stand for the whole prompt; the fixed strata are reported
+            uni = timed.get("uniform") or timed.get("ends") or timed["head"]
+            per_tok = float(np.mean(uni)) + t_cmp / nq
+            sample = (f"compression of all {w.seq} tokens; selection + attention of the rows "
+                      f"0..{2 * w.block - 1} ({len(timed.get('head', []))} rows), the block-end "
+                      f"rows of the last 8 blocks and the last row ({len(timed.get('ends', []))}), "
+                      f"and {len(timed.get('uniform', []))} seeded rows drawn uniformly from all "
+                      f"{nq}; tokens/s extrapolated from the uniform rows' mean time per row")
             value = 1.0 / per_tok
+            extra = {"extrapolated": True,
+                     "ms_per_row": {k2: round(1e3 * float(np.mean(v2)), 3) for k2, v2 in timed.items()}}
         else:
             done, t_seq = 0, 0.0
             order = np.random.default_rng(0).permutation(w.batch)
             for b in order:
                 s = S.decode_sequence(w, int(b), int(lens[b]))
                 L = int(lens[b])
-                t0 = time.perf_counter()
                 cmp = O.compress_keys(S.to_f64(s["ik"]), w.block)
-                cmp_t = time.perf_counter() - t0
                 t0 = time.perf_counter()
-                O.decode(S.to_f64(s["q"]), S.to_f64(s["k"]), S.to_f64(s["v"]), L,
-                         S.to_f64(s["iq"]), cmp, w.block, w.top_k, w.sm_scale)
+                r = O.decode(S.to_f64(s["q"]), S.to_f64(s["k"]), S.to_f64(s["v"]), L,
+                             S.to_f64(s["iq"]), cmp, w.block, w.top_k, w.sm_scale)
                 t_seq += time.perf_counter() - t0
+                scores = O.block_scores(S.to_f64(s["iq"]), cmp, O.candidate_blocks(L - 1, w.block))
+                ties += int(_tie_band(scores, w.top_k))
+                rows_scored += 1
                 done += 1
+                del r
                 if time.perf_counter() - t_start > budget_s:
                     break
             value = done / t_seq
             sample = (f"{done} of {w.batch} sequences (selection + attention per new token; the "
                       f"compressed indexer state is prepared untimed, as on the GPU)")
-    return {"value": round(value, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "host_cpus": os.cpu_count(), "blas_threads": 1}
+            extra = {"extrapolated": done < w.batch}
+    out = {"value": round(value, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": sample, "host_cpus": os.cpu_count(), "blas_threads": 1}
+    out.update(extra)
+    return out, {"rows": rows_scored, "frac": round(ties / max(rows_scored, 1), 4)}
+
+
+def run_calibration(mode: str, mib: int = 4096) -> int:
+    import torch
+    from block_sparse_attention_37_amd import calibrate as C
+    dev = torch.device("cuda:0")
+    res = C.measure_read_gbs(dev, mib) if mode == "read" else C.measure_mfma_tflops(dev)
+    print(json.dumps({"calibration": res}), flush=True)
+    return 0
 
 
 # ---------------------------------------------------------------------------
@@ -323,6 +415,10 @@ def main():
         return 2
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
+    if args.calibrate_read:
+        return run_calibration("read", args.calibrate_read)
+    if args.calibrate_mfma:
+        return run_calibration("mfma")
     import torch
     from block_sparse_attention_37_amd import synth as S
     w = S.WORKLOADS[args.workload]
@@ -346,6 +442,8 @@ def main():
         tokens = w.batch
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
+    print(f"[bench] {w.name}: inputs resident after {t_setup:.1f} s; warm-up", file=sys.stderr,
+          flush=True)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
@@ -364,53 +462,83 @@ def main():
         torch.cuda.synchronize()
         run_step, launches = g_step.replay, steps // per_graph
     else:
-        per_graph = 0
+        per_graph = 1
         run_step, launches = plan.run, steps
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(launches):
+    pairs = [(ev(), ev()) for _ in range(launches)]
+    for a, b in pairs:
+        a.record(stream)
         run_step()
-    end.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / steps
+    med, mean = median_ms(pairs)
+    ms_per_step, ms_per_step_mean = med / per_graph, mean / per_graph
+    print(f"[bench] timed {steps} steps: {ms_per_step:.4f} ms per step (median)", file=sys.stderr,
+          flush=True)
 
-    # Launch duration of the attention call for the roofline: `steps` back-to-back calls
-    # between two events on the stream the kernels run on (launch gaps amortised, so the
-    # figure compares with a profiler's per-kernel average duration).
+    # Launch duration of the attention call for the roofline: >= 20 replays of
+    # `per_att` back-to-back calls between two events each, on the stream the kernels run on
+    # (for short calls several per replay amortise the launch gaps, so the figure compares
+    # with a profiler's per-kernel average duration); the median replay.
+    reps = max(20, launches)
+    per_att = per_graph
     if args.graph:
-        g_rep = torch.cuda.CUDAGraph()  # the `steps` calls as one graph: no per-replay gaps
+        g_rep = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_rep):
-            for i in range(steps):
+            for i in range(per_att):
                 plan.run_attention()
         torch.cuda.synchronize()
         run_rep = g_rep.replay
     else:
         def run_rep():
-            for i in range(steps):
+            for i in range(per_att):
                 plan.run_attention()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
     run_rep()
-    a1.record(stream)
     torch.cuda.synchronize()
-    att_ms = a0.elapsed_time(a1) / steps
+    apairs = [(ev(), ev()) for _ in range(reps)]
+    for a, b in apairs:
+        a.record(stream)
+        run_rep()
+        b.record(stream)
+    torch.cuda.synchronize()
+    att_med, att_mean = median_ms(apairs)
+    att_ms = att_med / per_att
     value = tokens / (ms_per_step / 1e3)
+
+    calib = None
+    if not args.no_calibration:
+        from block_sparse_attention_37_amd import calibrate as C
+        calib = (C.measure_mfma_tflops(dev) if w.kind in ("prefill", "varlen")
+                 else C.measure_read_gbs(dev))
+        torch.cuda.synchronize()
 
     if w.kind in ("prefill", "varlen"):
         work = prefill_attention_flops(w, lens if w.kind == "varlen" else None)
         achieved = work / (att_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+        if calib:
+            roof["peak_measured"] = calib["TFLOP/s"]
+            roof["frac_of_measured"] = round(achieved / calib["TFLOP/s"], 4)
     else:
         work = decode_attention_bytes(w, lens)
         achieved = work / (att_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        if calib:
+            roof["peak_measured"] = calib["GB/s"]
+            roof["frac_of_measured"] = round(achieved / calib["GB/s"], 4)
+    if calib:
+        roof["calibration"] = calib
     counters = load_counters(w.name, w.kind)
     roof["traffic"] = counters.get("bytes_per_launch") if counters else None
+    if roof["traffic"] and w.kind in ("prefill", "varlen"):
+        roof["compulsory_bytes"] = compulsory_bytes(w, lens if w.kind == "varlen" else None)
+        roof["traffic_over_compulsory"] = round(roof["traffic"] / roof["compulsory_bytes"], 3)
+    elif roof["traffic"]:
+        roof["traffic_over_algorithmic"] = round(roof["traffic"] / work, 4)
     if counters and "mfma" in counters:
         roof["mfma_executed_over_algorithmic"] = counters["mfma"]["executed_over_algorithmic"]
         roof["mfma_busy_pct"] = counters["mfma"]["busy_pct"]
@@ -420,10 +548,13 @@ def main():
                       else "qsa::decode_bf16_kernel + qsa::decode_merge_kernel")
     roof["algorithmic_per_launch"] = work
     roof["kernel_ms"] = round(att_ms, 5)
+    roof["kernel_ms_mean"] = round(att_mean / per_att, 5)
+    roof["kernel_replays"] = reps
 
-    cpu = None
+    cpu, tie = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inps, lens, args.cpu_seconds)
+        print("[bench] oracle baseline on the host", file=sys.stderr, flush=True)
+        cpu, tie = cpu_baseline(w, inps, lens, args.cpu_seconds)
 
     cfg = {"workload": w.name, "kind": w.kind, "batch": w.batch, "block": w.block,
            "top_k": w.top_k, "h_q": w.h_q, "h_kv": w.h_kv, "d": w.d, "h_idx": w.h_idx,
@@ -455,10 +586,11 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_mean": round(ms_per_step_mean, 5), "timed_replays": launches,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded; see block_sparse_attention_37_amd/synth.py)",
         "config": cfg, "roofline": roof, "cpu_baseline": cpu,
-        "setup_s": round(t_setup, 1),
+        "tie_band_rows": tie, "setup_s": round(t_setup, 1),
     }
     print(json.dumps(line), flush=True)
     return 0

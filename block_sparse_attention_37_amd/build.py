@@ -2,8 +2,9 @@
 
     python -m block_sparse_attention_37_amd.build [--jobs N]
 
-Objects go to <repo>/_build/, the shared library to
-block_sparse_attention_37_amd/libqsa.so.  Every call recompiles.
+Objects go to <repo>/_build/, the shared libraries to block_sparse_attention_37_amd/:
+libqsa.so (the QSA path, include/qsa.h) and libqsa_calib.so (the calibration kernels the
+measurements are reported against, include/qsa_calibrate.h).  Every call recompiles.
 """
 from __future__ import annotations
 
@@ -20,9 +21,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
+CALIB_LIB = os.path.join(PKG, "libqsa_calib.so")
 
 SOURCES = ["qsa_api.hip", "k_compress.hip", "k_index.hip", "k_prefill.hip", "k_prefill_rt.hip",
            "k_decode.hip", "k_attn_f32.hip"]
+CALIB_SOURCES = ["calibrate.hip"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [
@@ -50,19 +53,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

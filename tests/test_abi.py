@@ -165,3 +165,20 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         Q.compress_keys(x, 16)
+
+
+def test_calibration_library_exports_its_header():
+    """libqsa_calib.so (the measurement kernels, not the QSA path) exports every function
+    include/qsa_calibrate.h declares, and its host checks refuse bad arguments."""
+    from block_sparse_attention_37_amd import calibrate as C
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qsa_calibrate.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(qsa_calib_[a-z_0-9]+)\s*\(", text)))
+    assert names
+    lib = C.lib()
+    for name in names:
+        assert hasattr(lib, name) and name in C.SIGNATURES, name
+    assert lib.qsa_calib_stream_read(None, 1024, FAKE, 1, None) == 1
+    assert lib.qsa_calib_stream_read(FAKE, 1000, FAKE, 1, None) == 1  # not a multiple of 16
+    assert lib.qsa_calib_mfma_bf16(0, 1, FAKE, None, None) == 1
+    assert lib.qsa_calib_mfma_sink_floats(2) == 1024

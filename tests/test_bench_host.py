@@ -9,7 +9,46 @@ def test_graph_steps_divides_and_caps():
     for steps in (1, 5, 7, 13, 20, 50, 200, 1000):
         s = bench.graph_steps(steps)
         assert steps % s == 0 and 1 <= s <= 16
-        assert all(steps % d for d in range(s + 1, min(16, steps) + 1))
+        assert steps // s >= min(20, steps)  # at least 20 timed replays when K allows it
+        # the largest such divisor
+        assert all(steps % d or steps // d < min(20, steps) for d in range(s + 1, min(16, steps) + 1))
+    assert bench.graph_steps(20) == 1 and bench.graph_steps(200) == 10
+
+
+class _Ev:
+    def __init__(self, t):
+        self.t = t
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+
+def test_median_of_event_pairs():
+    pairs = [(_Ev(0.0), _Ev(x)) for x in (5.0, 1.0, 3.0)]
+    assert bench.median_ms(pairs) == (3.0, 3.0)
+    pairs.append((_Ev(10.0), _Ev(17.0)))
+    assert bench.median_ms(pairs) == (4.0, 4.0)
+
+
+def test_baseline_rows_strata():
+    head, ends, rest = bench.baseline_rows(1000, 16, 4, seed=3)
+    assert head == list(range(32))
+    assert ends == [p for p in range(1000 - 128, 1000) if (p + 1) % 16 == 0] + [999]
+    assert sorted(head + ends + rest) == list(range(1000))  # every row once
+
+
+def test_tie_band_rule():
+    assert not bench._tie_band(np.array([3.0, 2.0, 1.0]), 3)       # every block kept
+    assert bench._tie_band(np.array([1.0, 0.9995, 0.0]), 1)         # gap 5e-4 relative
+    assert not bench._tie_band(np.array([1.0, 0.99, 0.0]), 1)       # gap 1e-2 relative
+
+
+def test_compulsory_bytes_of_prefill():
+    from block_sparse_attention_37_amd import synth as S
+    w = S.WORKLOADS["long_prefill_bf16_128k"]
+    T = w.seq
+    want = T * (32 * 128 * 2 * 2 + 64 * 4 + 32 * 4) + T * 4 * 128 * 2 * 2
+    assert bench.compulsory_bytes(w) == want
 
 
 def _brute(sel, pos, block, step):
