@@ -41,8 +41,11 @@ namespace {
 
 constexpr int KC = 64;   // keys per LDS chunk
 constexpr int NW = 8;    // waves per workgroup
-constexpr int NS = 4;    // LDS stages (chunks in flight + the one being used)
-constexpr int kNoSel = 0xFFFF;  // empty selection slot (block ids stay below kPrefillMaxBlocks)
+constexpr int NS = 4;    // LDS stages (chunks in flight + the one being used); a power of 2
+// Visibility words kept in LDS next to the 128 KB ring (one bit per position per union
+// block): every union block of a tile fits unless a tile holds more than 64 positions and a
+// very large union, which then goes through in windows of kVisWords / words-per-block blocks.
+constexpr int kVisWords = 7680;
 
 // LDS layout of one stage (byte offsets), chosen so that every operand read of a lane is
 // one base register plus an immediate and no read has a bank conflict (both checked with
@@ -67,11 +70,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   constexpr int NT = NW * 64;
   constexpr int PW = 32 / G;       // positions per wave
   constexpr int MQ = NW * PW;      // positions per workgroup
-  constexpr int KI = 2 * (D / 16) / NW;  // LDS-direct instructions per wave per K chunk
-  constexpr int VI = 4 * (D / 32) / NW;  // ... per V chunk
-  constexpr int DPC = KI + VI;           // per chunk
-  static_assert(KI * NW == 2 * (D / 16) && VI * NW == 4 * (D / 32), "load split");
+  constexpr int VW = (MQ + 31) / 32;       // visibility words per union block
+  constexpr int UW = kVisWords / VW;       // union blocks per visibility window
+  constexpr int KP = D / 8;        // 1 KB pieces of a K chunk (= of a V chunk)
+  constexpr int KI = KP / NW;      // K pieces per wave per chunk
+  constexpr int DPC = 2 * KI;      // LDS-direct instructions per wave per chunk (K + V)
+  static_assert(KI * NW == KP && KI >= 1, "load split");
+  static_assert(2 * DPC < 64, "vmcnt range");
   static_assert(KC == 64, "slab layout assumes 64-key chunks");
+  static_assert(32 % PW == 0, "a wave's positions share one visibility word");
   constexpr int NDT = D / 32;      // 32-wide d tiles of O^T
   constexpr int NKS = D / 16;      // k-steps of S^T = K . Q^T
 
@@ -80,8 +87,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // without the compiler draining the load queue before LDS reads.
   constexpr int TILE = KC * D;     // elements of one K (or V) chunk
   __shared__ __attribute__((aligned(16))) uint16_t ring[NS * 2 * TILE];
-  __shared__ uint16_t sel_s[kPrefillSelCap];       // [MQ][top_k]; block ids < 4096
-  __shared__ uint32_t bm[kPrefillMaxBlocks / 32];  // union bitmap
+  __shared__ uint32_t bm[kPrefillMaxBlocks / 32];     // union bitmap
+  __shared__ uint32_t wpre[kPrefillMaxBlocks / 32];   // union blocks below each bitmap word
+  __shared__ uint32_t vis_w[kVisWords];               // [union block of the window][VW]
 
   // ---- which tile: runs of consecutive tiles of one head share an XCD (L2), and every
   // XCD gets a share of every sequence (tile_order); tiles are dispatched from the end of
@@ -112,7 +120,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int wave = wave_uniform(tid >> 6);
 
   // ---- this lane's query row; its Q loads are issued first, so that their latency
-  // overlaps the selection rows' loads and the bitmap ----
+  // overlaps the selection rows' loads and the visibility build ----
   const int row = lane & 31;
   const int half = lane >> 5;
   const int pos = wave * PW + row / G;
@@ -120,7 +128,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   const int p = p0 + pos;
   const bool valid_row = p >= 0 && p < kv_len;
   const bool pad_row = p < 0 && q0 + pos < n_q;  // a padding row: zero output
-  const int own_block = (valid_row && (p + 1) % block != 0) ? p / block : -1;
   u32x4 qraw[NKS];
   {
     const uint16_t* qp = q + (((size_t)b * n_q + (valid_row ? p - p_off : 0)) * h_q + hh) * D + half * 8;
@@ -128,39 +135,63 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     for (int t = 0; t < NKS; ++t) qraw[t] = *reinterpret_cast<const u32x4*>(qp + t * 16);
   }
 
-  // ---- selection rows of the tile -> LDS; union bitmap ----
-  // Each row is compacted to its ids in [0, n(p)) in their given order, then kNoSel
-  // (one wave per row, ballot prefix counts), so the walk below never stops at an ignored id.
-  for (int r = wave; r < MQ; r += NW) {
-    const int pr = p0 + r;
-    const bool live = pr >= 0 && pr < kv_len;
-    const int np = live ? (pr + 1) / block : 0;
-    const int32_t* srow = sel + ((size_t)b * n_q + q0 + r) * top_k;
-    int base = 0;
-    for (int e0 = 0; e0 < top_k; e0 += 64) {
-      const int e = e0 + lane;
-      const int jj = (live && e < top_k) ? srow[e] : -1;
-      const bool ok = jj >= 0 && jj < np;
-      const uint64_t m = __ballot(ok);
-      if (ok) sel_s[r * top_k + base + __popcll(m & lanemask_lt())] = (uint16_t)jj;
-      base += __popcll(m);
-    }
-    for (int e = base + lane; e < top_k; e += 64) sel_s[r * top_k + e] = kNoSel;
-  }
+  // ---- the blocks the tile needs (union bitmap) and, per union block, which positions see
+  // it (visibility words).  A position sees block j iff j is one of its selection entries
+  // inside [0, n(p)) (any order; repeats and entries outside that range change nothing) or
+  // j is its own block with a non-empty trailing part.  The selection rows are read from
+  // global memory twice (L2): once for the bitmap, once for the words. ----
   for (int w = tid; w < max(words, 1); w += NT) bm[w] = 0u;
   __syncthreads();
-  for (int e = tid; e < MQ * top_k; e += NT) {
-    const int j = sel_s[e];
-    if (j != kNoSel) atomicOr(&bm[j >> 5], 1u << (j & 31));
-  }
-  if (tid < MQ) {
-    const int p = p0 + tid;
-    if (p >= 0 && p < kv_len && (p + 1) % block != 0) {
-      const int j = p / block;
-      atomicOr(&bm[j >> 5], 1u << (j & 31));
-    }
+  auto entry = [&](int e) __attribute__((always_inline)) {  // block of entry e, or -1
+    const int r = e / top_k;
+    const int pr = p0 + r;
+    if (pr < 0 || pr >= kv_len) return -1;
+    const int jj = sel[((size_t)b * n_q + q0 + r) * top_k + (e - r * top_k)];
+    return (jj >= 0 && jj < (pr + 1) / block) ? jj : -1;
+  };
+  auto own = [&](int r) __attribute__((always_inline)) {  // own block of position r, or -1
+    const int pr = p0 + r;
+    return (pr >= 0 && pr < kv_len && (pr + 1) % block != 0) ? pr / block : -1;
+  };
+  for (int e = tid; e < MQ * top_k + MQ; e += NT) {
+    const int j = e < MQ * top_k ? entry(e) : own(e - MQ * top_k);
+    if (j >= 0) atomicOr(&bm[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
+  if (wave == 0) {  // exclusive prefix counts of the bitmap words (two words per lane)
+    const int w0 = 2 * lane;
+    const uint32_t c0 = w0 < words ? __builtin_popcount(bm[w0]) : 0u;
+    const uint32_t c1 = w0 + 1 < words ? __builtin_popcount(bm[w0 + 1]) : 0u;
+    uint32_t incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const uint32_t excl = incl - c0 - c1;
+    if (w0 < words) wpre[w0] = excl;
+    if (w0 + 1 < words) wpre[w0 + 1] = excl + c0;
+  }
+  // union index of block j (j in the bitmap)
+  auto uidx = [&](int j) __attribute__((always_inline)) {
+    return (int)(wpre[j >> 5] + __builtin_popcount(bm[j >> 5] & ((1u << (j & 31)) - 1u)));
+  };
+  // visibility words of union blocks [win * UW, (win + 1) * UW)
+  auto build_vis = [&](int win) __attribute__((always_inline)) {
+    for (int i = tid; i < kVisWords; i += NT) vis_w[i] = 0u;
+    __syncthreads();
+    const int lo = win * UW;
+    for (int e = tid; e < MQ * top_k + MQ; e += NT) {
+      const int r = e < MQ * top_k ? e / top_k : e - MQ * top_k;
+      const int j = e < MQ * top_k ? entry(e) : own(r);
+      if (j >= 0) {
+        const int u = uidx(j) - lo;
+        if (u >= 0 && u < UW) atomicOr(&vis_w[u * VW + (r >> 5)], 1u << (r & 31));
+      }
+    }
+    __syncthreads();
+  };
+  build_vis(0);
 
   bf16x8 qreg[NKS];
 #pragma unroll
@@ -182,8 +213,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 
   const int nsub = (block + KC - 1) / KC;
   const uint32_t kv_row = (uint32_t)h_kv * D;  // elements between consecutive tokens
-  const uint16_t* kbase = k + ((size_t)b * kv_stride * h_kv + g) * D;
-  const uint16_t* vbase = v + ((size_t)b * kv_stride * h_kv + g) * D;
+  // K / V of this sequence and KV head, as scalar addresses
+  const uint64_t kbase = uniform_ptr(k + ((size_t)b * kv_stride * h_kv + g) * D);
+  const uint64_t vbase = uniform_ptr(v + ((size_t)b * kv_stride * h_kv + g) * D);
 
   // number of chunks the workgroup walks
   int nblk = 0;
@@ -195,36 +227,77 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   //     physical unit lane % 2) and fetches the logical unit the swap maps there.
   //  V: 4 per slab; piece part of slab dt holds rows 16*part .. +15, lane -> (row lane / 4,
   //     physical unit lane % 4).
-  // Wave w of group A issues the pieces of waves w and w + NW/2 (K pieces v*KI .. +KI-1
-  // and V pieces v*VI .. +VI-1 of wave v); group B issues none.  Rows past the chunk are
-  // clamped into the tensor (their keys are masked).
+  // Every wave issues its own KI K pieces and KI V pieces of each chunk at the start of its
+  // vector phase (both groups), from scalar base addresses, two instructions per save and
+  // restore of M0.  Rows past the sequence are clamped to its last key (their keys are
+  // masked).
   const uint32_t ring_lds = lds_addr(ring);
   ChunkIter it_load{0, (uint32_t)wave_uniform((int)bm[0]), -1, 0};
   next_block(bm, words, it_load);
   int issued = 0;
-  // chunk `issued` -> stage issued % NS
-  auto issue_next = [&]() __attribute__((always_inline)) {
+  int ld_key0 = 0;
+  uint32_t ld_st0 = 0;
+  const uint32_t kv_row_bytes = kv_row * 2u;
+  uint64_t ld_kb = 0, ld_vb = 0;  // byte addresses of the first K / V row of the chunk
+  bool ld_full = true;            // every row of the chunk lies inside the sequence
+  auto begin_chunk_load = [&]() __attribute__((always_inline)) {
+    ld_key0 = it_load.j * block + it_load.sub * KC;
+    ld_st0 = ring_lds + ((uint32_t)issued & (NS - 1)) * (2 * TILE * 2);
+    const uint64_t row0 = (uint64_t)(uint32_t)ld_key0 * kv_row_bytes;
+    ld_kb = kbase + row0;
+    ld_vb = vbase + row0;
+    ld_full = ld_key0 + KC <= kv_len;
+  };
+  // Piece i of this wave: row r_of(i) of the chunk and a byte offset lane_off[i] from the
+  // chunk's first row (K pieces first, then V pieces).  A chunk that lies inside the
+  // sequence is loaded from a scalar base (its first row) plus these fixed offsets, with no
+  // vector address arithmetic; the last chunk of a sequence clamps rows past its end to the
+  // last key (their scores are masked).
+  auto r_of = [&](int i) __attribute__((always_inline)) {
+    return i < KI ? 32 * ((wave * KI + i) & 1) + (lane >> 1)
+                  : 16 * ((wave * KI + i - KI) & 3) + (lane >> 2);
+  };
+  auto col_of = [&](int i) __attribute__((always_inline)) {
+    const int r = r_of(i);
+    return i < KI ? 16 * ((wave * KI + i) >> 1) + 8 * ((lane & 1) ^ k_unit_swap(r))
+                  : 32 * ((wave * KI + i - KI) >> 2) + 8 * ((lane & 3) ^ (2 * v_half_swap(r)));
+  };
+  auto lds_of = [&](int i) __attribute__((always_inline)) {  // byte offset inside a stage
+    return i < KI ? (uint32_t)(((wave * KI + i) >> 1) * 2048 + ((wave * KI + i) & 1) * 1024)
+                  : (uint32_t)(TILE * 2 + ((wave * KI + i - KI) >> 2) * 4096 +
+                               ((wave * KI + i - KI) & 3) * 1024);
+  };
+  uint32_t lane_off[DPC];
+#pragma unroll
+  for (int i = 0; i < DPC; ++i) lane_off[i] = (uint32_t)(r_of(i) * (int)kv_row + col_of(i)) * 2u;
+  // byte offset of piece i from the chunk's first row (rows past the sequence clamped)
+  auto piece_off = [&](int i) __attribute__((always_inline)) {
+    if (ld_full) return lane_off[i];
+    const int r = min(r_of(i), kv_len - 1 - ld_key0);
+    return (uint32_t)(r * (int)kv_row + col_of(i)) * 2u;
+  };
+  // pieces i (K) and KI + i (V): one instruction pair
+  auto load_pair = [&](int i) __attribute__((always_inline)) {
+    global_to_lds16x2_saddr_untracked(ld_kb, piece_off(i), ld_st0 + lds_of(i), ld_vb,
+                                      piece_off(KI + i), ld_st0 + lds_of(KI + i));
+  };
+  auto end_chunk_load = [&]() __attribute__((always_inline)) {
+    ++issued;
+    if (issued < n) advance(bm, words, nsub, it_load);
+  };
+  auto issue_whole = [&]() __attribute__((always_inline)) {
     if (issued < n) {
-      const int key0 = it_load.j * block + it_load.sub * KC;
-      const uint32_t st0 = ring_lds + (uint32_t)(issued % NS) * (2 * TILE * 2);
+      begin_chunk_load();
+      if (ld_full) {
 #pragma unroll
-      for (int i = 0; i < 2 * KI; ++i) {
-        const int id = (wave + (i / KI) * (NW / 2)) * KI + i % KI, t = id >> 1, part = id & 1;
-        const int r = 32 * part + (lane >> 1);
-        const int col = 16 * t + 8 * ((lane & 1) ^ k_unit_swap(r));
-        const uint32_t grow = (uint32_t)min(key0 + r, kv_len - 1);
-        global_to_lds16_untracked(kbase + grow * kv_row + col, st0 + t * 2048 + part * 1024);
-      }
+        for (int i = 0; i < KI; ++i)
+          global_to_lds16x2_saddr_untracked(ld_kb, lane_off[i], ld_st0 + lds_of(i), ld_vb,
+                                            lane_off[KI + i], ld_st0 + lds_of(KI + i));
+      } else {
 #pragma unroll
-      for (int i = 0; i < 2 * VI; ++i) {
-        const int id = (wave + (i / VI) * (NW / 2)) * VI + i % VI, dt = id >> 2, part = id & 3;
-        const int r = 16 * part + (lane >> 2);
-        const int col = 32 * dt + 8 * ((lane & 3) ^ (2 * v_half_swap(r)));
-        const uint32_t grow = (uint32_t)min(key0 + r, kv_len - 1);
-        global_to_lds16_untracked(vbase + grow * kv_row + col, st0 + TILE * 2 + dt * 4096 + part * 1024);
+        for (int i = 0; i < KI; ++i) load_pair(i);
       }
-      ++issued;
-      if (issued < n) advance(bm, words, nsub, it_load);
+      end_chunk_load();
     }
   };
 
@@ -241,7 +314,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // Ping-pong: waves 0 .. NW/2-1 (group A) and NW/2 .. NW-1 (group B) hold one wave per
   // SIMD each and run the same sequence of phases half a step apart:
   //   MFMA phase of chunk c:  S(c) = K(c) . Q^T  and  O += V(c-1)^T . P(c-1)
-  //   VALU phase of chunk c:  mask, row max, lazy rescale, P(c) = exp2(...), row sums
+  //   VALU phase of chunk c:  mask, row max, lazy rescale, P(c) = exp2(...), row sums, and
+  //                           this wave's loads of chunk c + 2 (A) or c + 3 (B)
   // Between two workgroup barriers one group runs an MFMA phase while the other runs a
   // VALU phase, so each SIMD has matrix work from one wave and vector work from the other.
   // S and P are single buffers: each phase consumes what the previous one of the same
@@ -252,8 +326,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   auto mfma_phase = [&](int c, bool do_s, bool do_pv) __attribute__((always_inline)) {
     // the wave in its matrix phase goes first when both waves of a SIMD can issue
     set_wave_priority<2>();
-    const char* Ks = reinterpret_cast<const char*>(ring + (c % NS) * (2 * TILE));
-    const char* Vp = reinterpret_cast<const char*>(ring + ((c + NS - 1) % NS) * (2 * TILE));
+    const char* Ks = reinterpret_cast<const char*>(ring + ((uint32_t)c & (NS - 1)) * (2 * TILE));
+    const char* Vp =
+        reinterpret_cast<const char*>(ring + ((uint32_t)(c + NS - 1) & (NS - 1)) * (2 * TILE));
     if (do_s) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -304,6 +379,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   // S holds the scores of a whole 64-key chunk; keys past the chunk (clamped rows, finite)
   // and keys after the row's position are masked.  Key 32*kt + 8*(r/4) + 4*half + r%4.
   auto valu_phase = [&](bool vis, int key0, int ck) __attribute__((always_inline)) {
+    // this wave's share of the chunk it fetches next (the address unit accepts them
+    // without stalling the wave)
+    issue_whole();
     if (ck < KC || key0 + KC - 1 > p0) {
       const int lim = min(ck - 1, p - key0) - 4 * half;
 #pragma unroll
@@ -312,93 +390,115 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         for (int r = 0; r < 16; ++r)
           if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) S[kt][r] = ninf;
     }
-    // row max: a tree over the lane's 32 scores (short dependency chains), then the other
-    // half of the row on lane ^ 32
-    // four chains of three-input maxima (v_max3) over 8 scores each
-    float c[4];
+    // P = exp2(scale * S - m_run) with the running max m_run as it stands, row sum into lsum.
+    // All exponent arguments first, then the exponentials, so that independent instructions
+    // separate each producer from its consumer.
+    float lsum = 0.f;
+    auto probabilities = [&]() __attribute__((always_inline)) {
+      const float nb = (vis && m_run != ninf) ? -m_run : ninf;
+      float e[32];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int k0 = g >> 1, r0 = 8 * (g & 1);
-      float x = fmaxf(fmaxf(S[k0][r0], S[k0][r0 + 1]), S[k0][r0 + 2]);
-      x = fmaxf(fmaxf(x, S[k0][r0 + 3]), S[k0][r0 + 4]);
-      x = fmaxf(fmaxf(x, S[k0][r0 + 5]), S[k0][r0 + 6]);
-      c[g] = fmaxf(x, S[k0][r0 + 7]);
+      for (int i = 0; i < 32; ++i) e[i] = __builtin_fmaf(S[i >> 4][i & 15], scale_log2, nb);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) e[i] = __builtin_amdgcn_exp2f(e[i]);
+      // B operand of 16-key step st: S registers 8*(st & 1) .. +7 of key tile st / 2
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int i0 = 16 * (st >> 1) + 8 * (st & 1);
+        P[st] = bitcast<bf16x8>(u32x4{pack_bf16x2(e[i0], e[i0 + 1]), pack_bf16x2(e[i0 + 2], e[i0 + 3]),
+                                      pack_bf16x2(e[i0 + 4], e[i0 + 5]), pack_bf16x2(e[i0 + 6], e[i0 + 7])});
+      }
+#pragma unroll
+      for (int w = 16; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) e[i] += e[i + w];
+      lsum = pair_sum(e[0]);
+    };
+    // The row max is taken only when needed: at a row's first visible chunk, or when the
+    // probabilities computed with the current m_run sum to more than 2^10 (then some score
+    // may exceed m_run by more than 10 in log2 units).  Otherwise every probability is at
+    // most 2^10 and the chunk keeps m_run.
+    const bool first = vis && m_run == ninf;
+    bool redo = __ballot(first) != 0ull;
+    if (!redo) {
+      probabilities();
+      redo = __ballot(vis && lsum > 1024.0f) != 0ull;
     }
-    const float mx = pair_max(fmaxf(fmaxf(fmaxf(c[0], c[1]), c[2]), c[3]));
-    // the running max moves only when it grows by more than 8 (log2 units): rare rescales,
-    // and every exponent stays <= 8
-    const float m_cand = vis ? fmaxf(m_run, mx * scale_log2) : m_run;
-    const bool need = m_cand > m_run + 8.0f;
-    if (__ballot(need) != 0ull) {
-      const float m_new = need ? m_cand : m_run;
-      // lanes that keep their max (possibly still -inf) keep their state exactly
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = m_new;
-      l_run *= alpha;
+    if (redo) {
+      // row max: a tree over the lane's 32 scores (short dependency chains), then the other
+      // half of the row on lane ^ 32; four chains of three-input maxima (v_max3)
+      float c[4];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int g = 0; g < 4; ++g) {
+        const int k0 = g >> 1, r0 = 8 * (g & 1);
+        float x = fmaxf(fmaxf(S[k0][r0], S[k0][r0 + 1]), S[k0][r0 + 2]);
+        x = fmaxf(fmaxf(x, S[k0][r0 + 3]), S[k0][r0 + 4]);
+        x = fmaxf(fmaxf(x, S[k0][r0 + 5]), S[k0][r0 + 6]);
+        c[g] = fmaxf(x, S[k0][r0 + 7]);
+      }
+      const float mx = pair_max(fmaxf(fmaxf(fmaxf(c[0], c[1]), c[2]), c[3]));
+      // the running max moves only when it grows by more than 8 (log2 units): rare
+      // rescales, and every exponent stays <= 8
+      const float m_cand = vis ? fmaxf(m_run, mx * scale_log2) : m_run;
+      const bool need = m_cand > m_run + 8.0f;
+      if (__ballot(need) != 0ull) {
+        const float m_new = need ? m_cand : m_run;
+        // lanes that keep their max (possibly still -inf) keep their state exactly
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+      }
+      probabilities();
     }
-    const float nb = (vis && m_run != ninf) ? -m_run : ninf;
-    // probabilities: all exponent arguments first, then the exponentials, so that
-    // independent instructions separate each producer from its consumer
-    float e[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) e[i] = __builtin_fmaf(S[i >> 4][i & 15], scale_log2, nb);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) e[i] = __builtin_amdgcn_exp2f(e[i]);
-    // B operand of 16-key step st: S registers 8*(st & 1) .. +7 of key tile st / 2
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int i0 = 16 * (st >> 1) + 8 * (st & 1);
-      P[st] = bitcast<bf16x8>(u32x4{pack_bf16x2(e[i0], e[i0 + 1]), pack_bf16x2(e[i0 + 2], e[i0 + 3]),
-                                    pack_bf16x2(e[i0 + 4], e[i0 + 5]), pack_bf16x2(e[i0 + 6], e[i0 + 7])});
-    }
-#pragma unroll
-    for (int w = 16; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; ++i) e[i] += e[i + w];
-    l_run += e[0];
+    // each half of the row holds the full sum (pair_sum); count it once per lane pair
+    l_run += half ? 0.f : lsum;
   };
 
-  // ---- selection walk: visibility of each chunk for this lane's row ----
+  // ---- visibility of each chunk for this lane's row: one word per union block ----
   ChunkIter it_vis{0, (uint32_t)wave_uniform((int)bm[0]), -1, 0};
-  int ptr = 0;
-  int cur_sel = valid_row ? sel_s[pos * top_k] : kNoSel;
+  int ub = -1;   // union index of the current block
+  int win = 0;   // visibility window held in vis_w
   bool vis = false;
+  const int vword = pos >> 5, vbit = pos & 31;
   auto visit = [&](bool first) __attribute__((always_inline)) {
     if (first) next_block(bm, words, it_vis);
     else advance(bm, words, nsub, it_vis);
     if (it_vis.sub == 0) {
-      const bool hit = (cur_sel == it_vis.j);
-      if (hit) {
-        ++ptr;
-        cur_sel = (ptr < top_k) ? sel_s[pos * top_k + ptr] : kNoSel;
+      ++ub;
+      if constexpr (UW < kPrefillMaxBlocks) {
+        if (ub >= (win + 1) * UW) {  // next window (only for very large unions): every
+          __syncthreads();           // wave has read the words of this one
+          ++win;
+          build_vis(win);
+        }
       }
-      vis = valid_row && (hit || it_vis.j == own_block);
+      vis = valid_row && ((vis_w[(ub - win * UW) * VW + vword] >> vbit) & 1u);
     }
   };
 
   // Chunk u: both groups meet barrier 1 (after chunk u has landed) and barrier 2.
-  //   group A:  barrier 1, MFMA phase u, loads of chunk u+2, barrier 2, VALU phase u
-  //   group B:  barrier 1, VALU phase u-1, barrier 2, MFMA phase u
+  //   group A:  barrier 1, MFMA phase u, barrier 2, VALU phase u (+ its loads of chunk u+2)
+  //   group B:  barrier 1, VALU phase u-1 (+ its loads of chunk u+2), barrier 2, MFMA phase u
   // followed by the O product of chunk n-1.  Chunk u+2 takes the stage of chunk u-2,
-  // whose last reader (the O product of group B in its MFMA phase u-1) ended before
-  // barrier 1 of chunk u.  Only group A issues loads, and only after its MFMA phase: the
-  // load queue accepts a chunk's 32 instructions slowly (about 600 cycles per chunk from
-  // L2), and issued by all waves at one barrier they stalled every wave.  Each group
-  // computes the visibility of chunk u+1 at the end of its iteration u, where the LDS
-  // reads of the selection walk complete while it waits at the next barrier.  The groups
-  // run separate loops with the same barriers, so each loop is straight-line code for the
-  // register allocator; each branch ends with its own tail and epilogue, so O needs no
-  // copies where the branches would meet.
+  // whose last readers (the O products of chunk u-2, in the MFMA phases u-1 of both
+  // groups) ended before barrier 1 of chunk u.  Each wave loads its own share of every
+  // chunk inside its vector phase, where a load instruction that waits for the address
+  // unit holds up only vector work of one wave while the other wave of its SIMD runs
+  // matrix work.  Each group computes the visibility of chunk u+1 at the end of its
+  // iteration u, where the LDS read completes while it waits at the next barrier.  The
+  // groups run separate loops with the same barriers, so each loop is straight-line code
+  // for the register allocator; each branch ends with its own tail and epilogue, so O
+  // needs no copies where the branches would meet.
   bool vis_prev = false, any_prev = false;
   int key0_prev = 0, ck_prev = 0;
   auto chunk_sync = [&](int u) __attribute__((always_inline)) {
-    // chunk u must have landed (group A waits for its own loads; group B has none); chunk
-    // u+1 may stay in flight
-    if (issued > u + 1) wait_vmcnt<2 * DPC>();
+    // chunk u must have landed (every wave waits for its own share); this wave's share of
+    // chunk u+1 may stay in flight
+    if (issued > u + 1) wait_vmcnt<DPC>();
     else wait_vmcnt<0>();
     barrier_no_fence();
   };
@@ -410,12 +510,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     ck_u = min(min(KC, block - it_vis.sub * KC), kv_len - key0_u);
     any_u = __ballot(vis) != 0ull;
   };
-  if (wave < NW / 2) {
-    issue_next();
-    issue_next();
-  }
+  // chunks 0 and 1: every wave issues its share
+  issue_whole();
+  issue_whole();
   auto epilogue = [&]() __attribute__((always_inline)) {
-    const float l_tot = pair_sum(l_run);
+    const float l_tot = pair_sum(l_run);  // the row's sum sits in its half-0 lane
     if (valid_row || pad_row) {
       const float inv = (valid_row && l_tot > 0.f) ? 1.f / l_tot : 0.f;
       const size_t orow = ((size_t)b * n_q + (q0 + pos)) * h_q + hh;
@@ -434,18 +533,18 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         lse[orow] = (valid_row && l_tot > 0.f) ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
     }
   };
-  // visibility of chunk u is computed at the end of iteration u-1, where its LDS reads
-  // complete during the barrier wait
-  bool vis_c, any_c;
-  int key0_c, ck_c;
+  // visibility of chunk u is computed at the end of iteration u-1, where its LDS read
+  // completes during the barrier wait
+  bool vis_c = false, any_c = false;
+  int key0_c = 0, ck_c = 0;
   if (n > 0) chunk_visit(0, vis_c, any_c, key0_c, ck_c);
   if (wave < NW / 2) {
     for (int u = 0; u < n; ++u) {
       chunk_sync(u);
       mfma_phase(u, any_c, any_prev);
-      issue_next();
       barrier_no_fence();
       if (any_c) valu_phase(vis_c, key0_c, ck_c);
+      else issue_whole();
       any_prev = any_c;
       if (u + 1 < n) chunk_visit(u + 1, vis_c, any_c, key0_c, ck_c);
     }
@@ -455,6 +554,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     for (int u = 0; u < n; ++u) {
       chunk_sync(u);
       if (any_prev) valu_phase(vis_prev, key0_prev, ck_prev);
+      else issue_whole();
       barrier_no_fence();
       mfma_phase(u, any_c, any_prev);
       vis_prev = vis_c;
@@ -467,7 +567,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     if (any_prev) mfma_phase(n, false, true);
     epilogue();
   }
-
 }
 
 bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len, int h_kv) {
@@ -477,7 +576,6 @@ bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len, 
   if (block < 1 || block > 1024 || top_k < 1 || top_k > kMaxTopK) return false;
   // element offsets of K / V rows within one sequence are 32-bit
   if ((long long)kv_len * h_kv * d >= (1ll << 32)) return false;
-  if ((long long)NW * (32 / group) * top_k > kPrefillSelCap) return false;
   return (kv_len + block - 1) / block <= kPrefillMaxBlocks;
 }
 

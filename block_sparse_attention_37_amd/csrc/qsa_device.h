@@ -104,6 +104,61 @@ __device__ __forceinline__ void global_to_lds16_untracked(const void* gptr, uint
   (void)lds_base;
 #endif
 }
+// Two 16-byte global -> LDS loads from scalar bases (as global_to_lds16_saddr_untracked),
+// sharing one save and restore of M0.
+__device__ __forceinline__ void global_to_lds16x2_saddr_untracked(uint64_t sbase0, uint32_t voff0,
+                                                                  uint32_t lds0, uint64_t sbase1,
+                                                                  uint32_t voff1, uint32_t lds1) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t saved;  // M0 is reserved by the compiler: restore it after use
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %4, %6\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds0)), "s"(__builtin_amdgcn_readfirstlane(lds1)),
+        "v"(voff0), "v"(voff1), "s"(sbase0), "s"(sbase1));
+#else
+  (void)sbase0; (void)voff0; (void)lds0; (void)sbase1; (void)voff1; (void)lds1;
+#endif
+}
+
+// A pointer every lane holds the same value of, moved to scalar registers.
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return ((uint64_t)hi << 32) | lo;
+#else
+  return reinterpret_cast<uint64_t>(p);
+#endif
+}
+
+// The same load with a scalar base: the lane reads sbase + voff (bytes; voff a 32-bit
+// per-lane offset), so a loop that moves the base per iteration spends no vector
+// instructions on addresses.
+__device__ __forceinline__ void global_to_lds16_saddr_untracked(const void* sbase, uint32_t voff,
+                                                                uint32_t lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t saved;  // M0 is reserved by the compiler: restore it after use
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(uniform_ptr(sbase)));
+#else
+  (void)sbase;
+  (void)voff;
+  (void)lds_base;
+#endif
+}
+
 __device__ __forceinline__ void wait_all_memory() {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_s_waitcnt(0);

@@ -159,9 +159,9 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
  *
  *   q, out   [batch, seq, h_q, d]   element type dt (out may not alias any input)
  *   k, v     [batch, seq, h_kv, d]  element type dt
- *   sel      [batch, seq, top_k] int32: per row, block ids < n(p) followed by -1 padding
- *            (exactly what qsa_index_topk writes); ids outside [0, n(p)) are ignored
- *            wherever they stand, and the ids inside it must be strictly ascending
+ *   sel      [batch, seq, top_k] int32: per row, the block ids of T(p) (qsa_index_topk
+ *            writes them ascending, then -1 padding); the kernels take them in any order,
+ *            and ignore repeats and ids outside [0, n(p))
  *   lse      [batch, seq, h_q] float32 output or NULL
  * Invalid: h_q % h_kv != 0, a non-finite sm_scale.  Any finite sm_scale is accepted (a
  * negative one ranks keys in reverse, zero gives every token of T(p) the same weight).
