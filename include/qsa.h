@@ -170,9 +170,9 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
  * float32.
  * Supported: d in {64, 128, 256} (256: the model page's default attention shape);
  * top_k <= 256; block in [1, 1024].  bf16 also needs G = h_q / h_kv in {1, 2, 4, 8, 16, 32},
- * T * top_k <= 8192 where T = 256 / G positions per tile for d <= 128 and
- * T = 128 / G (8 when G = 32) for d = 256 (the selection rows of a tile stay in LDS),
- * (seq + block - 1) / block <= 4096 and seq * h_kv * d < 2^32.
+ * (seq + block - 1) / block <= 4096 and seq * h_kv * d < 2^32; for d = 256 also
+ * T * top_k <= 8192 with T = 128 / G (8 when G = 32) positions per tile (the selection rows
+ * of a tile stay in LDS).
  */
 qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                    const int32_t* sel, void* out, float* lse,
