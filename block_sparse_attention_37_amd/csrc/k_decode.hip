@@ -27,6 +27,7 @@
 #include "qsa_internal.h"
 
 #include <climits>
+#include <mutex>
 
 namespace qsa {
 
@@ -387,6 +388,38 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
     return launch_decode_t<64>(q, k_cache, v_cache, kv_lens, sel, out, lse, batch, max_len, h_q,
                                h_kv, block, top_k, sm_scale, workspace, nsplit, stream);
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate device memory.  The
+// split-K partial results go to `scratch`, a file-scope device array of
+// kDecodeScratchBytes that every device holds from the library's load until the process
+// ends.  In host code `scratch` only names the symbol; its device address (one per device)
+// comes from hipGetSymbolAddress, looked up once per device with that device current and
+// kept in g_scratch_ptr.  Calls on one device share the array, so two calls in flight on
+// that device at once race; a split writes every partial it later reads, so nothing needs
+// clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
 }
 
 }  // namespace qsa

@@ -277,4 +277,29 @@ qsa_status qsa_sparse_attn_decode(const void* q, const void* k_cache, const void
                   "qsa_sparse_attn_decode");
 }
 
+qsa_status qsa_sparse_attn_decode_noalloc(const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* kv_lens,
+                                          const int32_t* sel, void* out, float* lse, int batch,
+                                          int max_len, int h_q, int h_kv, int d, int block,
+                                          int top_k, float sm_scale, qsa_dtype dt,
+                                          hipStream_t stream) {
+  size_t need = 0;
+  if (dt == QSA_BF16 && batch > 0 && h_q >= 1 && h_kv >= 1 && d >= 1 && block >= 1 &&
+      top_k >= 1) {
+    const int ns = qsa::decode_num_splits(batch, h_kv, block, top_k);
+    need = qsa::decode_workspace_bytes(batch, h_q, d, ns);
+    QSA_REQUIRE(need <= qsa::kDecodeScratchBytes, QSA_ERR_UNSUPPORTED,
+                "qsa_sparse_attn_decode_noalloc: these sizes need %zu bytes of scratch, more "
+                "than the %zu the library holds per device; use qsa_sparse_attn_decode with a "
+                "workspace", need, qsa::kDecodeScratchBytes);
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = qsa::decode_scratch(&ws);
+    if (e != hipSuccess) return from_hip(e, "qsa_sparse_attn_decode_noalloc (scratch address)");
+  }
+  return qsa_sparse_attn_decode(q, k_cache, v_cache, kv_lens, sel, out, lse, batch, max_len,
+                                h_q, h_kv, d, block, top_k, sm_scale, ws, need, dt, stream);
+}
+
 }  // extern "C"

@@ -59,6 +59,11 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const
 bool decode_bf16_supported(int group, int d, int block, int top_k, int max_len, int h_kv);
 int decode_num_splits(int batch, int h_kv, int block, int top_k);
 size_t decode_workspace_bytes(int batch, int h_q, int d, int nsplit);
+// Device scratch of the decode call that takes no workspace: kDecodeScratchBytes per
+// device, its address looked up once per device (hipGetSymbolAddress) with that device
+// current.  Returns the lookup's error, if any.
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* kv_lens, const int32_t* sel, void* out, float* lse,
                               int batch, int max_len, int h_q, int h_kv, int d, int block,

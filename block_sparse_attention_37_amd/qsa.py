@@ -43,6 +43,8 @@ SIGNATURES = {
     "qsa_sparse_attn_decode_workspace_size": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)]),
     "qsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                     _P, _Z, _I, _P]),
+    "qsa_sparse_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                            _I, _F, _I, _P]),
 }
 
 
@@ -312,6 +314,35 @@ def sparse_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     _call("qsa_sparse_attn_decode", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
           _ptr(sel), _ptr(out), _ptr(lse), batch, max_len, h_q, h_kv, d, block, top_k, scale,
           _ptr(workspace), workspace.numel(), _dt(q), _stream(dev))
+    return (out, lse) if lse is not None else out
+
+
+def sparse_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               kv_lens: torch.Tensor, sel: torch.Tensor, block: int,
+                               sm_scale: float | None = None, out: torch.Tensor | None = None,
+                               lse: torch.Tensor | None = None):
+    """sparse_attn_decode without a workspace: the library's own per-device scratch holds
+    the split partials (see qsa_sparse_attn_decode_noalloc in include/qsa.h).  ``out`` and
+    ``lse`` may be passed in so that the call itself allocates nothing."""
+    batch, h_q, d = q.shape
+    max_len, h_kv = k_cache.shape[1], k_cache.shape[2]
+    _expect(k_cache, (batch, max_len, h_kv, d), q.dtype, "k_cache")
+    _expect(v_cache, (batch, max_len, h_kv, d), q.dtype, "v_cache")
+    _expect(kv_lens, (batch,), torch.int32, "kv_lens")
+    if sel.dim() == 3:
+        sel = sel.reshape(batch, sel.shape[2])
+    top_k = sel.shape[1]
+    _expect(sel, (batch, top_k), torch.int32, "sel")
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, "out")
+    if lse is not None:
+        _expect(lse, (batch, h_q), torch.float32, "lse")
+    dev = _dev(q, k_cache, v_cache, kv_lens, sel, out, lse)
+    _call("qsa_sparse_attn_decode_noalloc", _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_lens),
+          _ptr(sel), _ptr(out), _ptr(lse), batch, max_len, h_q, h_kv, d, block, top_k, scale,
+          _dt(q), _stream(dev))
     return (out, lse) if lse is not None else out
 
 

@@ -261,6 +261,25 @@ qsa_status qsa_sparse_attn_decode(const void* q, const void* k_cache, const void
                                   void* workspace, size_t workspace_bytes,
                                   qsa_dtype dt, hipStream_t stream);
 
+/*
+ * qsa_sparse_attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as qsa_sparse_attn_decode, whose
+ * workspace this call takes from a device array the library holds: 8 MiB per device, from
+ * the library's load until the process ends (its address is looked up once per device, on
+ * the first call with that device current).  Sizes whose workspace
+ * (qsa_sparse_attn_decode_workspace_size) exceeds 8 MiB give QSA_ERR_UNSUPPORTED; nothing
+ * here allocates.  All calls on one device share that array: two of them in flight at once
+ * on the same device (on different streams, or from different threads without ordering)
+ * race and give unspecified results.
+ */
+qsa_status qsa_sparse_attn_decode_noalloc(const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* kv_lens,
+                                          const int32_t* sel, void* out, float* lse,
+                                          int batch, int max_len, int h_q, int h_kv, int d,
+                                          int block, int top_k, float sm_scale,
+                                          qsa_dtype dt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
