@@ -30,8 +30,8 @@ time per step (the mean is reported beside it).
 ``roofline`` describes the dominant kernel (the attention kernel): algorithmic
 flops (prefill, bf16 matrix cores) or algorithmic bytes (decode, HBM) per launch
 divided by its median launch time, measured with events recorded on the stream the
-kernels run on around each of >= 20 replays of back-to-back attention calls that follow
-the timed steps.  ``frac`` is against the vendor peak, ``frac_of_measured`` against the
+kernels run on around each of >= 20 replays of back-to-back attention calls (enough calls
+per replay for ~5 ms of kernel time, at most 16) that follow the timed steps.  ``frac`` is against the vendor peak, ``frac_of_measured`` against the
 rate the calibration kernel of the same resource sustains in the same run
 (``--no-calibration`` skips it).  ``traffic`` is the HBM byte count per launch from the
 committed profiler counter summary of the workload (null when the attention kernel's
@@ -483,7 +483,14 @@ def main():
     # (for short calls several per replay amortise the launch gaps, so the figure compares
     # with a profiler's per-kernel average duration); the median replay.
     reps = max(20, launches)
-    per_att = per_graph
+    # back-to-back calls per replay: enough for ~5 ms of kernel time (at most 16), so that
+    # launch gaps of short calls are amortised whatever the step count
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    plan.run_attention()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per_att = int(min(16, max(1, round(5.0 / max(t0.elapsed_time(t1), 1e-3)))))
     if args.graph:
         g_rep = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_rep):
@@ -550,6 +557,7 @@ def main():
     roof["kernel_ms"] = round(att_ms, 5)
     roof["kernel_ms_mean"] = round(att_mean / per_att, 5)
     roof["kernel_replays"] = reps
+    roof["kernel_calls_per_replay"] = per_att
 
     cpu, tie = None, None
     if not args.no_cpu_baseline:
