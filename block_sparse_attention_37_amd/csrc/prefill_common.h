@@ -40,11 +40,15 @@ __device__ __forceinline__ bool advance(const uint32_t* bm, int words, int nsub,
 // Dispatch order of the prefill tiles.  Workgroup ids go to the 8 XCDs round-robin
 // (wg % 8); this gives each XCD runs of kTileRun consecutive logical tiles, then moves on
 // to the next XCD, so neighbouring tiles (which select many of the same blocks) share an
-// L2 while every XCD gets an even share of every sequence and KV head.  (Giving each XCD
-// one contiguous eighth of the grid instead put whole sequences of a varlen batch, or
-// whole ranges of positions, on one XCD: measured 1.45 ms vs 0.88 ms on 8 prompts of
-// mixed length, 27.3 ms vs 23.8 ms at 128k.)  A permutation of [0, total).
-constexpr int kTileRun = 4;
+// L2 while every XCD gets an even share of every sequence and KV head.  A run of 32 tiles
+// fills the 32 CUs of an XCD with neighbours: at 128k the L2 misses of the attention
+// kernel (FETCH_SIZE) measured 20.5 GB per launch with runs of 4, 15.5 GB with 16,
+// 11.8 GB with 32, 15.4 GB with 64 and 18.4 GB with 128, at 23.5, 23.55, 23.7, 24.5 and
+// 25.65 ms; at 4k, 72, 78 and 72 us for runs of 4, 16 and 32.  (Giving each XCD one
+// contiguous eighth of the grid instead put whole sequences of a varlen batch, or whole
+// ranges of positions, on one XCD: measured 1.45 ms vs 0.88 ms on 8 prompts of mixed
+// length, 27.3 ms vs 23.8 ms at 128k.)  A permutation of [0, total).
+constexpr int kTileRun = 32;
 __device__ __forceinline__ int tile_order(int wg, int total) {
   const int full = total / (8 * kTileRun) * (8 * kTileRun);
   if (wg >= full) return wg;
