@@ -11,7 +11,7 @@
 //   * A wave holds RT tiles of 16 query rows on 16x16x32 MFMAs: RT = 1 (2 when G = 32, one
 //     position of 32 heads).  Per lane that is O^T 16 x f32x4 and Q^T 8 x bf16x8 per tile.
 //   * Chunks are 32 keys (a stage is 16 KB of K and 16 KB of V), so four stages fit 128 KB
-//     of LDS next to the selection rows.
+//     of LDS next to the union bitmap and the visibility words.
 //   * S^T = K . Q^T (A = K rows from LDS, B = Q^T in registers): lane l holds keys
 //     16*kt + 4*(l/16) + {0..3} of query row l % 16.  O^T = V^T . P^T (A = V^T through the
 //     transpose read, B = P^T straight from the S^T accumulators, keys permuted identically
@@ -29,7 +29,11 @@ namespace {
 constexpr int RT_KC = 32;  // keys per LDS chunk
 constexpr int RT_NW = 8;   // waves per workgroup
 constexpr int RT_NS = 4;   // LDS stages
-constexpr int kRtNoSel = 0xFFFF;
+// Visibility words kept in LDS next to the 128 KB ring (one bit per position per union
+// block): every union block of a tile fits when a tile holds at most 32 positions; larger
+// tiles (G = 1, 2) with very large unions go through in windows of kRtVisWords /
+// words-per-block blocks.
+constexpr int kRtVisWords = 7680;
 
 // 16-row MFMA tiles per wave.
 template <int G>
@@ -78,10 +82,14 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
   static_assert(KI * (NW / 2) == KP && VI * (NW / 2) == VP, "load split");
   static_assert(2 * DPC < 64, "vmcnt range");
 
+  constexpr int VW = (MQ + 31) / 32;      // visibility words per union block
+  constexpr int UW = kRtVisWords / VW;    // union blocks per visibility window
+
   constexpr int TILE = KC * D;  // elements of one K (or V) chunk
   __shared__ __attribute__((aligned(16))) uint16_t ring[NS * 2 * TILE];
-  __shared__ uint16_t sel_s[kPrefillSelCap];       // [MQ][top_k]
-  __shared__ uint32_t bm[kPrefillMaxBlocks / 32];  // union bitmap
+  __shared__ uint32_t bm[kPrefillMaxBlocks / 32];    // union bitmap
+  __shared__ uint32_t wpre[kPrefillMaxBlocks / 32];  // union blocks below each bitmap word
+  __shared__ uint32_t vis_w[kRtVisWords];            // [union block of the window][VW]
 
   // ---- tile order as in the 32-row kernel (tile_order: runs of consecutive tiles per
   // XCD), heaviest (last) tiles first ----
@@ -131,39 +139,63 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
     for (int t = 0; t < NKT; ++t) qraw[rt][t] = *reinterpret_cast<const u32x4*>(qp + t * 32);
   }
 
-  // ---- selection rows of the tile -> LDS; union bitmap ----
-  // Each row is compacted to its ids in [0, n(p)) in their given order, then kRtNoSel
-  // (one wave per row, ballot prefix counts), so the walk below never stops at an ignored id.
-  for (int r = wave; r < MQ; r += NW) {
-    const int pr = p0 + r;
-    const bool live = pr >= 0 && pr < kv_len;
-    const int np = live ? (pr + 1) / block : 0;
-    const int32_t* srow = sel + ((size_t)b * n_q + q0 + r) * top_k;
-    int base = 0;
-    for (int e0 = 0; e0 < top_k; e0 += 64) {
-      const int e = e0 + lane;
-      const int jj = (live && e < top_k) ? srow[e] : -1;
-      const bool ok = jj >= 0 && jj < np;
-      const uint64_t m = __ballot(ok);
-      if (ok) sel_s[r * top_k + base + __popcll(m & lanemask_lt())] = (uint16_t)jj;
-      base += __popcll(m);
-    }
-    for (int e = base + lane; e < top_k; e += 64) sel_s[r * top_k + e] = kRtNoSel;
-  }
+  // ---- the blocks the tile needs (union bitmap) and, per union block, which positions see
+  // it (visibility words).  A position sees block j iff j is one of its selection entries
+  // inside [0, n(p)) (any order; entries outside that range change nothing) or j is its
+  // own block with a non-empty trailing part.  The selection rows are read from global
+  // memory twice (L2): once for the bitmap, once for the words. ----
   for (int w = tid; w < max(words, 1); w += NT) bm[w] = 0u;
   __syncthreads();
-  for (int e = tid; e < MQ * top_k; e += NT) {
-    const int j = sel_s[e];
-    if (j != kRtNoSel) atomicOr(&bm[j >> 5], 1u << (j & 31));
-  }
-  if (tid < MQ) {
-    const int p = p0 + tid;
-    if (p >= 0 && p < kv_len && (p + 1) % block != 0) {
-      const int j = p / block;
-      atomicOr(&bm[j >> 5], 1u << (j & 31));
-    }
+  auto entry = [&](int e) __attribute__((always_inline)) {  // block of entry e, or -1
+    const int r = e / top_k;
+    const int pr = p0 + r;
+    if (pr < 0 || pr >= kv_len) return -1;
+    const int jj = sel[((size_t)b * n_q + q0 + r) * top_k + (e - r * top_k)];
+    return (jj >= 0 && jj < (pr + 1) / block) ? jj : -1;
+  };
+  auto own = [&](int r) __attribute__((always_inline)) {  // own block of position r, or -1
+    const int pr = p0 + r;
+    return (pr >= 0 && pr < kv_len && (pr + 1) % block != 0) ? pr / block : -1;
+  };
+  for (int e = tid; e < MQ * top_k + MQ; e += NT) {
+    const int j = e < MQ * top_k ? entry(e) : own(e - MQ * top_k);
+    if (j >= 0) atomicOr(&bm[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
+  if (wave == 0) {  // exclusive prefix counts of the bitmap words (two words per lane)
+    const int w0 = 2 * lane;
+    const uint32_t c0 = w0 < words ? __builtin_popcount(bm[w0]) : 0u;
+    const uint32_t c1 = w0 + 1 < words ? __builtin_popcount(bm[w0 + 1]) : 0u;
+    uint32_t incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const uint32_t excl = incl - c0 - c1;
+    if (w0 < words) wpre[w0] = excl;
+    if (w0 + 1 < words) wpre[w0 + 1] = excl + c0;
+  }
+  // union index of block j (j in the bitmap)
+  auto uidx = [&](int j) __attribute__((always_inline)) {
+    return (int)(wpre[j >> 5] + __builtin_popcount(bm[j >> 5] & ((1u << (j & 31)) - 1u)));
+  };
+  // visibility words of union blocks [win * UW, (win + 1) * UW)
+  auto build_vis = [&](int win) __attribute__((always_inline)) {
+    for (int i = tid; i < kRtVisWords; i += NT) vis_w[i] = 0u;
+    __syncthreads();
+    const int lo = win * UW;
+    for (int e = tid; e < MQ * top_k + MQ; e += NT) {
+      const int r = e < MQ * top_k ? e / top_k : e - MQ * top_k;
+      const int j = e < MQ * top_k ? entry(e) : own(r);
+      if (j >= 0) {
+        const int u = uidx(j) - lo;
+        if (u >= 0 && u < UW) atomicOr(&vis_w[u * VW + (r >> 5)], 1u << (r & 31));
+      }
+    }
+    __syncthreads();
+  };
+  build_vis(0);
 
   bf16x8 qreg[RT][NKT];
 #pragma unroll
@@ -371,31 +403,29 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
     }
   };
 
-  // ---- selection walk: visibility of each chunk for this lane's rows ----
+  // ---- visibility of each chunk for this lane's rows: one word per union block ----
   ChunkIter it_vis{0, (uint32_t)wave_uniform((int)bm[0]), -1, 0};
-  int ptr[RT], cur_sel[RT];
+  int ub = -1;   // union index of the current block
+  int win = 0;   // visibility window held in vis_w
   bool vis[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    ptr[rt] = 0;
-    cur_sel[rt] = valid_of(rt) ? sel_s[pos_of(rt) * top_k] : kRtNoSel;
-    vis[rt] = false;
-  }
+  for (int rt = 0; rt < RT; ++rt) vis[rt] = false;
   auto visit = [&](bool first) __attribute__((always_inline)) {
     if (first) next_block(bm, words, it_vis);
     else advance(bm, words, nsub, it_vis);
     if (it_vis.sub == 0) {
-      const int key0 = it_vis.j * block;
+      ++ub;
+      if constexpr (UW < kPrefillMaxBlocks) {
+        if (ub >= (win + 1) * UW) {  // next window (only for very large unions): every
+          __syncthreads();           // wave has read the words of this one
+          ++win;
+          build_vis(win);
+        }
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const bool hit = (cur_sel[rt] == it_vis.j);
-        if (hit) {
-          ++ptr[rt];
-          cur_sel[rt] = (ptr[rt] < top_k) ? sel_s[pos_of(rt) * top_k + ptr[rt]] : kRtNoSel;
-        }
-        // own block: p inside it and not its last token (a non-empty trailing part)
-        const int p = p_of(rt);
-        vis[rt] = hit || (p >= 0 && p < kv_len && p >= key0 && p <= key0 + block - 2);
+        const int ps = pos_of(rt);
+        vis[rt] = valid_of(rt) && ((vis_w[(ub - win * UW) * VW + (ps >> 5)] >> (ps & 31)) & 1u);
       }
     }
   };
@@ -450,7 +480,8 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
   //   group B:  barrier 1, VALU phase u-1, barrier 2, MFMA phase u
   // then the O product of chunk n-1.  Chunk u+2 takes the stage of chunk u-2, last read by
   // group B's O product in its MFMA phase u-1, before barrier 1 of chunk u.  The
-  // visibility of chunk u+1 is computed at the end of iteration u.
+  // visibility of chunk u+1 is computed at the end of iteration u, in both groups (any
+  // rebuild of the visibility window, a workgroup barrier, comes at the same point).
   bool vis_c[RT], vis_prev[RT];
   bool any_c = false, any_prev = false;
   int key0_c = 0, ck_c = 0, key0_prev = 0, ck_prev = 0;
@@ -497,8 +528,6 @@ bool prefill_bf16_rt_supported(int group, int d, int block, int top_k, int kv_le
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16 && group != 32) return false;
   if (block < 1 || block > 1024 || top_k < 1 || top_k > kMaxTopK) return false;
   if ((long long)kv_len * h_kv * d >= (1ll << 32)) return false;  // 32-bit element offsets
-  const int mq = RT_NW * (group == 32 ? 1 : 16 / group);
-  if ((long long)mq * top_k > kPrefillSelCap) return false;
   return (kv_len + block - 1) / block <= kPrefillMaxBlocks;
 }
 

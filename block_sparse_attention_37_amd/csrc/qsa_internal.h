@@ -29,9 +29,8 @@ hipError_t launch_index_topk_decode(const void* iq, const void* ik, float* cmp,
                                     int block, int top_k, bool bf16, hipStream_t stream);
 
 // bf16 prefill on matrix cores.  Returns hipErrorInvalidValue for shapes it is not built for.
-// A workgroup keeps the selection rows of its query positions (positions x top_k entries)
-// and a bitmap of the blocks it visits in LDS.
-constexpr int kPrefillSelCap = 8192;
+// A workgroup keeps a bitmap of the blocks it visits in LDS, and per visited block one bit
+// per query position.
 constexpr int kPrefillMaxBlocks = 4096;
 bool prefill_bf16_supported(int group, int d, int block, int top_k, int kv_len, int h_kv);
 // n_q query rows at positions kv_len - n_q .. kv_len - 1 over kv_len keys, where kv_len is

@@ -159,9 +159,9 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
  *
  *   q, out   [batch, seq, h_q, d]   element type dt (out may not alias any input)
  *   k, v     [batch, seq, h_kv, d]  element type dt
- *   sel      [batch, seq, top_k] int32: per row, the block ids of T(p) (qsa_index_topk
- *            writes them ascending, then -1 padding); the kernels take them in any order,
- *            and ignore repeats and ids outside [0, n(p))
+ *   sel      [batch, seq, top_k] int32: per row, the distinct block ids of T(p)
+ *            (qsa_index_topk writes them ascending, then -1 padding); the kernels take
+ *            them in any order and ignore ids outside [0, n(p))
  *   lse      [batch, seq, h_q] float32 output or NULL
  * Invalid: h_q % h_kv != 0, a non-finite sm_scale.  Any finite sm_scale is accepted (a
  * negative one ranks keys in reverse, zero gives every token of T(p) the same weight).
@@ -170,9 +170,7 @@ qsa_status qsa_index_topk_decode(const void* iq, const void* ik_cache, float* cm
  * float32.
  * Supported: d in {64, 128, 256} (256: the model page's default attention shape);
  * top_k <= 256; block in [1, 1024].  bf16 also needs G = h_q / h_kv in {1, 2, 4, 8, 16, 32},
- * (seq + block - 1) / block <= 4096 and seq * h_kv * d < 2^32; for d = 256 also
- * T * top_k <= 8192 with T = 128 / G (8 when G = 32) positions per tile (the selection rows
- * of a tile stay in LDS).
+ * (seq + block - 1) / block <= 4096 and seq * h_kv * d < 2^32.
  */
 qsa_status qsa_sparse_attn_prefill(const void* q, const void* k, const void* v,
                                    const int32_t* sel, void* out, float* lse,

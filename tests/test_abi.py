@@ -114,11 +114,9 @@ def test_prefill_validation(qsa_lib):
     assert call(lse=FAKE + 4) == INVALID
     assert call(h_q=48, h_kv=1) == UNSUPPORTED  # group 48 not built for bf16
     assert call(seq=0) == 0
-    # head dim 256: accepted; its tile of 128 / G positions caps top_k at 64 when G = 1
+    # head dim 256: accepted; no head dim keeps selection rows in LDS, so any top_k <= 256
     assert call(d=256, seq=0) == 0
     assert call(d=192) == UNSUPPORTED
-    assert call(d=256, h_q=2, h_kv=2, top_k=65) == UNSUPPORTED
-    # (head dims 64 and 128 keep no selection rows in LDS: any top_k <= 256 is accepted)
     chunk = lambda n_q, kv_len: L.qsa_sparse_attn_prefill_chunk(
         FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, n_q, kv_len, 8, 2, 128, 16, 4, 0.1, 1, None)
     assert chunk(200, 100) == INVALID

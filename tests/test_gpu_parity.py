@@ -102,6 +102,8 @@ EDGE_PREFILL = [
     _wl("d256_default_heads", seq=300, block=32, top_k=3, h_q=16, h_kv=2, d=256, h_idx=4,
         d_idx=64, query_mean=True, plant_frac=0.1),
     _wl("d256_g1", seq=70, block=16, top_k=2, h_q=2, h_kv=2, d=256),
+    # 128 positions per tile x 80 selection entries per row (more than 8192 per tile)
+    _wl("d256_g1_topk80", seq=3000, block=16, top_k=80, h_q=2, h_kv=2, d=256),
     _wl("d256_g32", seq=50, block=16, top_k=2, h_q=32, h_kv=1, d=256),
     _wl("d256_g16_block100", seq=260, block=100, top_k=1, h_q=16, h_kv=1, d=256),
     _wl("f32_d256", seq=40, block=16, top_k=2, h_q=4, h_kv=2, d=256, dtype="f32"),
@@ -277,25 +279,27 @@ def test_prefill_softmax_scale_sign(gpu, case):
     assert e_lse <= LSE_ATOL[w.dtype] and e_dlse <= LSE_ATOL[w.dtype]
 
 
-def test_prefill_selection_ids_ignored_anywhere(gpu):
+@pytest.mark.parametrize("d", [128, 256])
+def test_prefill_selection_ids_ignored_anywhere(gpu, d):
     """Selection rows with ids outside [0, n(p)) in front of, between and after the valid
-    ascending ids (as a caller may pass them): the attention kernels ignore them wherever
-    they stand and attend over the valid ids, like the oracle given only the valid ids."""
-    w = _wl("sel_noise", seq=400, block=16, top_k=6, h_q=8, h_kv=2, d=128)
+    ids, which stand in descending order (as a caller may pass them): the attention
+    kernels ignore the outside ids wherever they stand, take the valid ones in any order,
+    and attend like the oracle given only the valid ids."""
+    w = _wl("sel_noise", seq=400, block=16, top_k=6, h_q=8, h_kv=2, d=d)
     T, B = w.seq, w.block
-    say("case prefill selection ids outside [0, n(p))")
+    say(f"case prefill selection ids outside [0, n(p)), valid ids descending, d={d}")
     inp = S.prefill_inputs(w)
     t = {key: _t(x, gpu)[None] for key, x in inp.items()}
     cmp = Q.compress_keys(t["ik"], B)
     sel = Q.index_topk(t["iq"], cmp, B, 3)
-    # [-1, a, 9999, b, c, -5]: the valid ids (a, b, c) ascending, noise around them
+    # [-1, c, 9999, b, a, -5]: the valid ids (a < b < c) descending, noise around them
     s3 = sel[0].cpu().numpy()
     noisy = np.full((T, w.top_k), -1, dtype=np.int32)
     noisy[:, 0] = -1
-    noisy[:, 1] = s3[:, 0]
+    noisy[:, 1] = s3[:, 2]
     noisy[:, 2] = 9999
     noisy[:, 3] = s3[:, 1]
-    noisy[:, 4] = s3[:, 2]
+    noisy[:, 4] = s3[:, 0]
     noisy[:, 5] = -5
     out = Q.sparse_attn_prefill(t["q"], t["k"], t["v"], torch.from_numpy(noisy)[None].to(gpu), B,
                                 w.sm_scale)
@@ -313,6 +317,8 @@ LARGE_UNION = [
     # holds (960 and 1920 blocks), so the kernel rebuilds them window by window
     (_wl("union_g1_d64", seq=20000, block=16, top_k=16, h_q=2, h_kv=2, d=64), 256, 960),
     (_wl("union_g2_d128", seq=50000, block=16, top_k=48, h_q=4, h_kv=2, d=128), 128, 1920),
+    # head dim 256, G = 1: tiles of 128 positions, 1920 blocks per window
+    (_wl("union_g1_d256", seq=50000, block=16, top_k=48, h_q=2, h_kv=2, d=256), 128, 1920),
 ]
 
 
