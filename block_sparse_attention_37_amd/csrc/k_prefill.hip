@@ -17,10 +17,11 @@
 //     NS stages: while chunk u is multiplied, chunks u+1 .. u+NS-1 are in flight.  Every
 //     chunk is shared by the NW waves (256 MFMA rows), which sets the flops per byte of L2
 //     traffic.
-//   * Per row visibility of a block: the lane walks its position's ascending selection
-//     list in step with the union (one compare per block), or the block is the
-//     position's own block with a non-empty trailing part; keys after p are masked
-//     (causal part of the trailing block).  A wave with no visible row skips the block.
+//   * Per row visibility of a block: one bit per position per union block (visibility
+//     words, built in the prologue from the selection rows: a selected id inside [0, n(p)),
+//     in any order, or the position's own block when its trailing part is non-empty); keys
+//     after p are masked (causal part of the trailing block).  A wave with no visible row
+//     skips the block.
 //   * Transposed products keep one query row per lane:  S^T = K . Q^T  (A = K rows from
 //     LDS, B = Q^T held in registers) and  O^T = V^T . P^T  (A = V^T gathered from the
 //     row-major V tile by the LDS transpose read ds_read_b64_tr_b16, B = P^T taken straight
@@ -238,12 +239,16 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   int ld_key0 = 0;
   uint32_t ld_st0 = 0;
   const uint32_t kv_row_bytes = kv_row * 2u;
-  uint64_t ld_kb = 0, ld_vb = 0;  // byte addresses of the first K / V row of the chunk
+  uint64_t ld_kb = 0, ld_vb = 0;  // byte addresses of the base K / V row of the chunk
+  int ld_base = 0;                // that row: the chunk's first key, clamped to the last one
   bool ld_full = true;            // every row of the chunk lies inside the sequence
   auto begin_chunk_load = [&]() __attribute__((always_inline)) {
     ld_key0 = it_load.j * block + it_load.sub * KC;
     ld_st0 = ring_lds + ((uint32_t)issued & (NS - 1)) * (2 * TILE * 2);
-    const uint64_t row0 = (uint64_t)(uint32_t)ld_key0 * kv_row_bytes;
+    // a chunk may start past the last key (the tail of a block longer than a chunk): it then
+    // reads the last key into every row (all of its scores are masked)
+    ld_base = min(ld_key0, kv_len - 1);
+    const uint64_t row0 = (uint64_t)(uint32_t)ld_base * kv_row_bytes;
     ld_kb = kbase + row0;
     ld_vb = vbase + row0;
     ld_full = ld_key0 + KC <= kv_len;
@@ -270,10 +275,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
   uint32_t lane_off[DPC];
 #pragma unroll
   for (int i = 0; i < DPC; ++i) lane_off[i] = (uint32_t)(r_of(i) * (int)kv_row + col_of(i)) * 2u;
-  // byte offset of piece i from the chunk's first row (rows past the sequence clamped)
+  // byte offset of piece i from the base row (rows past the sequence clamped to its last
+  // key; never below the base row, so the unsigned offset cannot wrap)
   auto piece_off = [&](int i) __attribute__((always_inline)) {
     if (ld_full) return lane_off[i];
-    const int r = min(r_of(i), kv_len - 1 - ld_key0);
+    const int r = min(ld_key0 + r_of(i), kv_len - 1) - ld_base;
     return (uint32_t)(r * (int)kv_row + col_of(i)) * 2u;
   };
   // pieces i (K) and KI + i (V): one instruction pair

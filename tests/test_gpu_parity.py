@@ -114,6 +114,36 @@ EDGE_PREFILL = [
 ]
 
 
+def _random_shapes(n=24, seed=2024):
+    """Seeded random small shapes over everything the bf16 and fp32 paths accept: head dim,
+    group size, KV heads, block size (multiples of 64 and not), top_k (also beyond the
+    number of blocks), indexer heads and dim, and lengths from one token up."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        h_kv = int(rng.choice([1, 2]))
+        block = int(rng.choice([16, 32, 48, 64, 100, 128]))
+        out.append(_wl(f"rand{i:02d}_d{d}_g{G}_b{block}", seed=300 + i,
+                       dtype="f32" if i % 6 == 5 else "bf16", seq=int(rng.integers(1, 640)),
+                       block=block, top_k=int(rng.integers(1, 10)), h_q=G * h_kv, h_kv=h_kv,
+                       d=d, h_idx=int(rng.integers(1, 6)), d_idx=int(rng.choice([32, 64, 128])),
+                       query_mean=bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_shapes(), ids=lambda w: w.name)
+def test_prefill_random_shapes(gpu, w):
+    """Compression, selection (every row, R10) and attention (every row, R11/R12) of a seeded
+    random shape against the oracle."""
+    say(f"case prefill {w.name}: seq={w.seq} k={w.top_k} heads={w.h_q}/{w.h_kv} "
+        f"indexer={w.h_idx}x{w.d_idx} {w.dtype}")
+    inp = S.prefill_inputs(w)
+    res = gpu_prefill(w, [inp], gpu)
+    check_prefill(w, inp, res)
+
+
 @pytest.mark.parametrize("w", EDGE_PREFILL, ids=lambda w: w.name)
 def test_prefill_edge_shapes(gpu, w):
     say(f"case prefill {w.name}")
