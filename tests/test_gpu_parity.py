@@ -210,7 +210,28 @@ VARLEN_PREFILL = [
 ]
 
 
-@pytest.mark.parametrize("case", VARLEN_PREFILL, ids=lambda c: c[0].name)
+def _random_varlen(n=10, seed=4048):
+    """Seeded random varlen batches: 1-5 prompts of lengths 0..700 (some longer than n_q,
+    which then covers their last n_q tokens), block sizes that are and are not multiples
+    of 64, head dims 64/128/256, group sizes 1-32, bf16 and fp32."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        h_kv = int(rng.choice([1, 2]))
+        lens = [int(x) for x in rng.integers(0, 700, size=int(rng.integers(1, 6)))]
+        n_q = int(rng.integers(1, max(lens) + 2))
+        out.append((_wl(f"rvarlen{i:02d}_d{d}_g{G}", seed=500 + i, seq=0,
+                        dtype="f32" if i % 5 == 4 else "bf16",
+                        block=int(rng.choice([8, 16, 32, 64, 96, 128])),
+                        top_k=int(rng.integers(1, 8)), h_q=G * h_kv, h_kv=h_kv, d=d,
+                        h_idx=int(rng.integers(1, 5)), d_idx=int(rng.choice([32, 64, 128])),
+                        query_mean=bool(rng.integers(0, 2))), lens, n_q))
+    return out
+
+
+@pytest.mark.parametrize("case", VARLEN_PREFILL + _random_varlen(), ids=lambda c: c[0].name)
 def test_prefill_varlen(gpu, case):
     """A batch of prompts of their own lengths through compress (kv_lens), index (kv_lens,
     n_q) and qsa_sparse_attn_prefill_varlen: every valid row against the oracle run on
@@ -651,7 +672,29 @@ EDGE_DECODE = [
 ]
 
 
-@pytest.mark.parametrize("case", EDGE_DECODE, ids=lambda c: c[0].name)
+def _random_decode(n=14, seed=6064):
+    """Seeded random decode batches: 1-6 sequences of lengths 1..max_len, group sizes 1-16,
+    1-4 KV heads, head dims 64/128/256, block sizes that are and are not multiples of 64,
+    top_k from 1 to beyond the number of blocks (one split or several), bf16 and fp32."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        h_kv = int(rng.choice([1, 2, 4]))
+        batch = int(rng.integers(1, 7))
+        max_len = int(rng.integers(1, 3000))
+        lens = [int(x) for x in rng.integers(1, max_len + 1, size=batch)]
+        out.append((_dw(f"rdecode{i:02d}_d{d}_g{G}", seed=700 + i, batch=batch,
+                        max_len=max_len, dtype="f32" if i % 7 == 6 else "bf16",
+                        block=int(rng.choice([16, 32, 64, 100, 128])),
+                        top_k=int(rng.integers(1, 48)), h_q=G * h_kv, h_kv=h_kv, d=d,
+                        h_idx=int(rng.integers(1, 5)), d_idx=int(rng.choice([32, 64, 128]))),
+                    lens))
+    return out
+
+
+@pytest.mark.parametrize("case", EDGE_DECODE + _random_decode(), ids=lambda c: c[0].name)
 def test_decode_edge_shapes(gpu, case):
     w, lens = case
     lens = np.array(lens, dtype=np.int32)
