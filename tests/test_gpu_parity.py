@@ -133,7 +133,22 @@ def _random_shapes(n=24, seed=2024):
     return out
 
 
-@pytest.mark.parametrize("w", _random_shapes(), ids=lambda w: w.name)
+def _random_long_shapes(n=6, seed=9090):
+    """Longer seeded random prompts (1500..6000 tokens: many tiles, unions of tens of blocks,
+    independent or shared indexer queries)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        out.append(_wl(f"rlong{i:02d}_d{d}_g{G}", seed=1100 + i, seq=int(rng.integers(1500, 6000)),
+                       block=int(rng.choice([16, 32, 64, 128])), top_k=int(rng.integers(4, 40)),
+                       h_q=G, h_kv=1, d=d, h_idx=int(rng.integers(1, 5)),
+                       d_idx=int(rng.choice([32, 64, 128])), query_mean=bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_shapes() + _random_long_shapes(), ids=lambda w: w.name)
 def test_prefill_random_shapes(gpu, w):
     """Compression, selection (every row, R10) and attention (every row, R11/R12) of a seeded
     random shape against the oracle."""
@@ -164,7 +179,26 @@ CHUNK_PREFILL = [
 ]
 
 
-@pytest.mark.parametrize("case", CHUNK_PREFILL, ids=lambda c: c[0].name)
+def _random_chunks(n=8, seed=8080):
+    """Seeded random chunks: the last n_q (1..seq) tokens of a random prompt (up to 1500
+    tokens) over all of it, head dims 64/128/256, groups 1-32, bf16 and fp32."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        h_kv = int(rng.choice([1, 2]))
+        seq = int(rng.integers(1, 1500))
+        out.append((_wl(f"rchunk{i:02d}_d{d}_g{G}", seed=900 + i, seq=seq,
+                        dtype="f32" if i % 4 == 3 else "bf16",
+                        block=int(rng.choice([16, 32, 64, 100, 128])),
+                        top_k=int(rng.integers(1, 12)), h_q=G * h_kv, h_kv=h_kv, d=d,
+                        h_idx=int(rng.integers(1, 5)), d_idx=int(rng.choice([32, 64, 128])),
+                        query_mean=bool(rng.integers(0, 2))), int(rng.integers(1, seq + 1))))
+    return out
+
+
+@pytest.mark.parametrize("case", CHUNK_PREFILL + _random_chunks(), ids=lambda c: c[0].name)
 def test_prefill_chunk(gpu, case):
     """Chunked prefill: the last n_q tokens over the whole sequence (query i at
     p = kv_len - n_q + i), selection by qsa_index_topk with kv_lens, attention by
