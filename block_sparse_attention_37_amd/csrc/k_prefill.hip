@@ -14,9 +14,9 @@
 //     plus the own blocks of positions whose trailing part is non-empty), kept as a
 //     bitmap in LDS and visited in ascending order.  Each block is streamed through LDS in
 //     chunks of 64 keys.  K and V rows go global -> LDS directly (no registers) through
-//     NS stages: while chunk u is multiplied, chunks u+1 .. u+NS-1 are in flight.  Every
-//     chunk is shared by the NW waves (256 MFMA rows), which sets the flops per byte of L2
-//     traffic.
+//     NS = 4 stages: while chunk u is multiplied (and the V of chunk u-1 still read),
+//     chunks u+1 and u+2 are in flight.  Every chunk is shared by the NW waves (256 MFMA
+//     rows), which sets the flops per byte of L2 traffic.
 //   * Per row visibility of a block: one bit per position per union block (visibility
 //     words, built in the prologue from the selection rows: a selected id inside [0, n(p)),
 //     in any order, or the position's own block when its trailing part is non-empty); keys
@@ -27,9 +27,11 @@
 //     row-major V tile by the LDS transpose read ds_read_b64_tr_b16, B = P^T taken straight
 //     from the S^T accumulators; the key order inside an MFMA step is permuted identically
 //     on both operands).  Row max and sum need one exchange with lane ^ 32.
-//   * Online softmax in base 2 with the scale folded into one FMA per score; the running
-//     max is raised only when it grows by more than 8 (log2 units), so rescaling the
-//     accumulators is rare and every exponent stays <= 8.
+//   * Online softmax in base 2 with the scale folded into one FMA per score.  A chunk's
+//     probabilities are computed with the running max as it stands; the chunk's row max is
+//     taken only for a row's first visible chunk or when the probabilities sum past 2^10,
+//     and the running max is raised only when it grows by more than 8 (log2 units), so
+//     rescaling the accumulators is rare and every probability stays <= 2^10.
 #include "prefill_common.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"

@@ -337,9 +337,40 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
     set_wave_priority<0>();
   };
 
+  // P = exp2(score * scale - running max) for this lane's 4-key groups of the chunk, with the
+  // running max as it stands; this lane's share of each row's sum into lpart.
+  auto probabilities = [&](const bool* vis, float* lpart) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float nb = (vis[rt] && m_run[rt] != ninf) ? -m_run[rt] : ninf;
+      f32x4 e[NKB];
+#pragma unroll
+      for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[kt][r] = __builtin_fmaf(S[kt][rt][r], scale_log2, nb);
+#pragma unroll
+      for (int kt = 0; kt < NKB; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[kt][r] = __builtin_amdgcn_exp2f(e[kt][r]);
+      f32x4 sum = e[0];
+#pragma unroll
+      for (int kt = 1; kt < NKB; ++kt) sum += e[kt];
+      lpart[rt] = (sum[0] + sum[1]) + (sum[2] + sum[3]);
+#pragma unroll
+      for (int ps = 0; ps < NPS; ++ps) {
+        const f32x4 a = e[2 * ps], c = e[2 * ps + 1];
+        P[ps][rt] = bitcast<bf16x8>(u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                          pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])});
+      }
+    }
+  };
   // VALU phase of the chunk at key0 with ck valid keys: mask (keys past the chunk or after
-  // the row's position), row max over the row's four lanes, lazy rescale (the running max
-  // moves only when it grows by more than 8 in log2 units), P = exp2(score * scale - max).
+  // the row's position), then the probabilities with the running max as it stands.  The
+  // row max over the row's four lanes is taken only when needed: at a row's first visible
+  // chunk, or when some lane's share of a row's probabilities exceeds 2^8 (so the row's
+  // sum may exceed 2^10 and a score the running max by more than 10 in log2 units); the
+  // chunk is then done again after a lazy rescale (the running max moves only when it grows
+  // by more than 8), so every probability stays <= 2^10.
   auto valu_phase = [&](const bool* vis, int key0, int ck) __attribute__((always_inline)) {
     if (ck < KC || key0 + KC - 1 > p0) {
 #pragma unroll
@@ -352,55 +383,50 @@ __global__ __launch_bounds__(RT_NW * 64, 1) void prefill_bf16_rt_kernel(
             if (16 * kt + r > lim) S[kt][rt][r] = ninf;
       }
     }
-    bool need[RT];
-    float m_new[RT];
-    bool any_need = false;
+    float lpart[RT];
+    bool first = false;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float mx = ninf;
+    for (int rt = 0; rt < RT; ++rt) first |= vis[rt] && m_run[rt] == ninf;
+    bool redo = __ballot(first) != 0ull;
+    if (!redo) {
+      probabilities(vis, lpart);
+      bool big = false;
 #pragma unroll
-      for (int kt = 0; kt < NKB; ++kt)
-        mx = fmaxf(fmaxf(mx, fmaxf(S[kt][rt][0], S[kt][rt][1])), fmaxf(S[kt][rt][2], S[kt][rt][3]));
-      mx = quad_max(mx);
-      const float m_cand = vis[rt] ? fmaxf(m_run[rt], mx * scale_log2) : m_run[rt];
-      need[rt] = m_cand > m_run[rt] + 8.0f;
-      m_new[rt] = need[rt] ? m_cand : m_run[rt];
-      any_need |= need[rt];
+      for (int rt = 0; rt < RT; ++rt) big |= vis[rt] && lpart[rt] > 256.0f;
+      redo = __ballot(big) != 0ull;
     }
-    if (__ballot(any_need) != 0ull) {
+    if (redo) {
+      bool need[RT];
+      float m_new[RT];
+      bool any_need = false;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        // lanes that keep their max (possibly still -inf) keep their state exactly
-        const float alpha = need[rt] ? __builtin_amdgcn_exp2f(m_run[rt] - m_new[rt]) : 1.0f;
-        l_run[rt] *= alpha;
+        float mx = ninf;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) O[dt][rt] *= alpha;
+        for (int kt = 0; kt < NKB; ++kt)
+          mx = fmaxf(fmaxf(mx, fmaxf(S[kt][rt][0], S[kt][rt][1])), fmaxf(S[kt][rt][2], S[kt][rt][3]));
+        mx = quad_max(mx);
+        const float m_cand = vis[rt] ? fmaxf(m_run[rt], mx * scale_log2) : m_run[rt];
+        need[rt] = m_cand > m_run[rt] + 8.0f;
+        m_new[rt] = need[rt] ? m_cand : m_run[rt];
+        any_need |= need[rt];
       }
+      if (__ballot(any_need) != 0ull) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          // lanes that keep their max (possibly still -inf) keep their state exactly
+          const float alpha = need[rt] ? __builtin_amdgcn_exp2f(m_run[rt] - m_new[rt]) : 1.0f;
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) O[dt][rt] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) m_run[rt] = m_new[rt];
+      probabilities(vis, lpart);
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      m_run[rt] = m_new[rt];
-      const float nb = (vis[rt] && m_run[rt] != ninf) ? -m_run[rt] : ninf;
-      f32x4 e[NKB];
-#pragma unroll
-      for (int kt = 0; kt < NKB; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) e[kt][r] = __builtin_fmaf(S[kt][rt][r], scale_log2, nb);
-#pragma unroll
-      for (int kt = 0; kt < NKB; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) e[kt][r] = __builtin_amdgcn_exp2f(e[kt][r]);
-      f32x4 s = e[0];
-#pragma unroll
-      for (int kt = 1; kt < NKB; ++kt) s += e[kt];
-      l_run[rt] += (s[0] + s[1]) + (s[2] + s[3]);
-#pragma unroll
-      for (int ps = 0; ps < NPS; ++ps) {
-        const f32x4 a = e[2 * ps], c = e[2 * ps + 1];
-        P[ps][rt] = bitcast<bf16x8>(u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                                          pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])});
-      }
-    }
+    for (int rt = 0; rt < RT; ++rt) l_run[rt] += lpart[rt];
   };
 
   // ---- visibility of each chunk for this lane's rows: one word per union block ----
