@@ -552,7 +552,7 @@ def main():
     # the attention call: one kernel for prefill; split kernel + merge kernel for decode
     roof["kernel"] = (("qsa::prefill_bf16_rt_kernel" if w.d == 256 else "qsa::prefill_bf16_kernel")
                       if w.kind in ("prefill", "varlen")
-                      else "qsa::decode_bf16_kernel + qsa::decode_merge_kernel")
+                      else "qsa::decode_bf16_kernel + qsa::decode_merge_few_kernel (2-4 splits) or qsa::decode_merge_kernel")
     roof["algorithmic_per_launch"] = work
     roof["kernel_ms"] = round(att_ms, 5)
     roof["kernel_ms_mean"] = round(att_mean / per_att, 5)

@@ -305,6 +305,66 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   if (lse && d == 0) lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
+// The same combination with one wave per (sequence, query head) for NSP = 2 .. 4 splits: each
+// lane takes D / 64 consecutive elements, and every load of the partial results is issued
+// before any of them is used, so the kernel waits for memory once.  Per element the
+// arithmetic is that of decode_merge_kernel.
+template <int D, int NSP>
+__global__ __launch_bounds__(64) void decode_merge_few_kernel(const float* __restrict__ ws_o,
+                                                             const float* __restrict__ ws_lse,
+                                                             uint16_t* __restrict__ out,
+                                                             float* __restrict__ lse) {
+  constexpr int E = D / 64;
+  static_assert(E == 1 || E == 2 || E == 4, "elements per lane");
+  const size_t bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  float ls[NSP];
+  float o[NSP][E];
+#pragma unroll
+  for (int s = 0; s < NSP; ++s) ls[s] = ws_lse[bh * NSP + s];
+#pragma unroll
+  for (int s = 0; s < NSP; ++s) {
+    const float* src = ws_o + (bh * NSP + s) * D + lane * E;
+    if constexpr (E == 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[s][e] = x[e];
+    } else if constexpr (E == 2) {
+      const f32x2_t x = *reinterpret_cast<const f32x2_t*>(src);
+      o[s][0] = x[0];
+      o[s][1] = x[1];
+    } else {
+      o[s][0] = *src;
+    }
+  }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < NSP; ++s) M = fmaxf(M, ls[s]);
+  const float Mu = (M == -__builtin_inff()) ? 0.f : M;
+  float L = 0.f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < NSP; ++s) {
+    const float f = __builtin_amdgcn_exp2f(ls[s] - Mu);
+    L += f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += f * o[s][e];
+  }
+  uint32_t bits[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) bits[e] = f32_to_bf16(L > 0.f ? acc[e] / L : 0.f);
+  uint16_t* dst = out + bh * D + lane * E;
+  if constexpr (E == 4) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+  } else if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(dst) = bits[0] | (bits[1] << 16);
+  } else {
+    *dst = (uint16_t)bits[0];
+  }
+  if (lse && lane == 0) lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+}
+
 bool decode_bf16_supported(int group, int d, int block, int top_k, int max_len, int h_kv) {
   if (d != 64 && d != 128 && d != 256) return false;
   if (group < 1 || group > 16) return false;
@@ -367,8 +427,15 @@ static hipError_t launch_decode_t(const void* q, const void* k_cache, const void
                      h_q / h_kv, block, top_k, sm_scale * kLog2e, nsplit);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nsplit == 1) return err;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(batch * h_q), dim3(D), 0, stream, ws_o,
-                     ws_lse, static_cast<uint16_t*>(out), lse, nsplit);
+  uint16_t* o16 = static_cast<uint16_t*>(out);
+  const dim3 rows(batch * h_q);
+  switch (nsplit) {
+    case 2: hipLaunchKernelGGL((decode_merge_few_kernel<D, 2>), rows, dim3(64), 0, stream, ws_o, ws_lse, o16, lse); break;
+    case 3: hipLaunchKernelGGL((decode_merge_few_kernel<D, 3>), rows, dim3(64), 0, stream, ws_o, ws_lse, o16, lse); break;
+    case 4: hipLaunchKernelGGL((decode_merge_few_kernel<D, 4>), rows, dim3(64), 0, stream, ws_o, ws_lse, o16, lse); break;
+    default:
+      hipLaunchKernelGGL((decode_merge_kernel<D>), rows, dim3(D), 0, stream, ws_o, ws_lse, o16, lse, nsplit);
+  }
   return hipGetLastError();
 }
 
