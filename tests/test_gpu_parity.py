@@ -738,6 +738,30 @@ def test_decode_edge_shapes(gpu, case):
     check_decode(w, lens, res, keep)
 
 
+def _merge_cases():
+    """Small batches split each (sequence, KV head) up to chunks / 4 times: with 64-token
+    blocks, top_k = 8, 12, 16, 20 gives 2, 3, 4, 5 splits (the one-wave merge for 2-4, the
+    general merge beyond), at head dims 64, 128, 256 (1, 2, 4 elements per lane)."""
+    out = []
+    for d in (64, 128, 256):
+        for ns, top_k in ((2, 8), (3, 12), (4, 16), (5, 20)):
+            out.append((_dw(f"merge_d{d}_s{ns}", seed=900 + d + ns, batch=2, max_len=1400,
+                            block=64, top_k=top_k, h_q=16, h_kv=2, d=d), [1379, 1300], ns))
+    return out
+
+
+@pytest.mark.parametrize("case", _merge_cases(), ids=lambda c: c[0].name)
+def test_decode_merge_split_counts(gpu, case):
+    w, lens, nsplit = case
+    lens = np.array(lens, dtype=np.int32)
+    say(f"case decode {w.name} lens={lens.tolist()} splits={nsplit}")
+    ws = Q.decode_workspace_bytes(w.batch, w.h_q, w.h_kv, w.d, w.block, w.top_k)
+    assert ws == w.batch * w.h_q * nsplit * (w.d + 1) * 4, "split count"
+    *tensors, keep = gpu_decode_setup(w, lens, gpu)
+    res = gpu_decode(w, lens, tensors)
+    check_decode(w, lens, res, keep)
+
+
 def test_decode_matches_prefill_rows(gpu):
     """Decode at kv_len = p+1 reproduces prefill row p (both on the GPU)."""
     w = _wl("pd", seq=300, block=32, top_k=3, h_q=8, h_kv=2, d=128)
